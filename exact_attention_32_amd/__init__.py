@@ -1,1 +1,132 @@
-"""MI355X (gfx950) fused exact-attention forward: Python binding over the C-ABI library."""
+"""MI355X (gfx950) fused exact-attention forward.
+
+A thin binding over the C-ABI library ``libattn_fwd.so`` (declared in
+``include/attn.h``): argument checks, output allocation and marshalling only;
+every step of the computation runs in the library's HIP kernels.  PyTorch
+provides device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
+
+ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise AttnError(f"HIP library not built: {path} (run exact_attention_32_amd.build.build())")
+    L = ctypes.CDLL(path)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.attn_fwd.restype = ci
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    L.attn_fwd_fp8.restype = ci
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_status_string.argtypes = [ci]
+    L.attn_fwd_plan.restype = ci
+    L.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci] + [ctypes.POINTER(ci)] * 4
+    if path == LIB_PATH:
+        _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return load_library().attn_status_string(int(code)).decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AttnError(f"attn: {status_string(rc)} (status {rc})")
+
+
+def plan(B, H, S_q, S_k, d, causal=False, dtype=ATTN_BF16):
+    """(queries per workgroup, keys per tile, waves per workgroup, workgroups) the library launches."""
+    out = [ctypes.c_int() for _ in range(4)]
+    _check(load_library().attn_fwd_plan(B, H, S_q, S_k, d, int(bool(causal)), dtype, *[ctypes.byref(x) for x in out]))
+    return tuple(x.value for x in out)
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, d]")
+    B, H, S_q, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
+    return B, H, S_q, k.shape[2], d
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: float | None = None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Exact attention forward for fp16 / bf16 tensors [B, H, S, d] -> (O, LSE).
+
+    O has q's dtype; LSE is fp32 [B, H, S_q] (natural log), or None if want_lse is False.
+    """
+    B, H, S_q, S_k, d = _shapes(q, k, v)
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if q.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    elif q.dtype == torch.float16:
+        dt = ATTN_F16
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    rc = load_library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None, B, H, S_q, S_k, d,
+                                 int(bool(causal)), float(scale), dt, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scale: float | None = None,
+            out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
+    """Block-scaled fp8 (OCP E4M3 codes, uint8 or float8_e4m3fn) attention -> (O bf16, LSE fp32)."""
+    B, H, S_q, S_k, d = _shapes(q, k, v)
+    for t in (q, k, v):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError("fp8 inputs must be uint8 codes or float8_e4m3fn")
+    for t, s in ((q_descale, S_q), (k_descale, S_k), (v_descale, S_k)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (B, H, (s + 127) // 128):
+            raise ValueError("descales must be contiguous fp32 device tensors [B, H, ceil(S/128)]")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty((B, H, S_q, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    rc = load_library().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(),
+                                     k_descale.data_ptr(), v_descale.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None, B, H, S_q, S_k, d,
+                                     int(bool(causal)), float(scale), _stream(q.device))
+    _check(rc)
+    return out, lse

@@ -1,0 +1,100 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused exact-attention forward library.
+ *
+ * Operation (the attention that the FlashAttention-3 deep dive (techknowgenie)
+ * introduces and computes with I/O-aware tiling plus an online softmax, so
+ * that the S_q x S_k score matrix never reaches HBM; section 2 lists the
+ * per-key-block steps: scores, running max/sum update, output accumulation):
+ *
+ *   O[b,h,i,:] = sum_j softmax_j( scale * q[b,h,i,:] . k[b,h,j,:] ) * v[b,h,j,:]
+ *   LSE[b,h,i] = log sum_j exp( scale * q[b,h,i,:] . k[b,h,j,:] )      (natural log)
+ *
+ * with j over all keys, or, when causal != 0, over the keys j <= i only
+ * (top-left aligned: query i sees keys 0..i whatever S_q and S_k are).
+ *
+ * Layout: q and o are [B][H][S_q][d]; k and v are [B][H][S_k][d]; lse is
+ * [B][H][S_q] fp32.  All dense, row-major, d fastest.  All pointers are
+ * device pointers.
+ *
+ * Ownership: the caller allocates and owns every buffer.  The library keeps no
+ * per-call state, allocates nothing and is re-entrant.  Calls are asynchronous
+ * on `stream` (a hipStream_t; NULL means the default stream); the results are
+ * ready when that stream has reached the launch.  With a given build the
+ * results are deterministic (no atomics).
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * on any error nothing is launched and o/lse are untouched.  The guards follow
+ * the host-side checks that the FlashInfer KDA write-up (blog.secrett2633)
+ * describes in its section 3 (16-byte base alignment, 32-bit index range).
+ */
+#ifndef EXACT_ATTENTION_32_AMD_ATTN_H
+#define EXACT_ATTENTION_32_AMD_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_F16 = 0,       /* q, k, v, o are IEEE binary16 */
+    ATTN_BF16 = 1,      /* q, k, v, o are bfloat16 */
+    ATTN_FP8_E4M3 = 2   /* q, k, v are OCP E4M3 codes (unit descales), o is bfloat16 */
+} attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,         /* q, k, v or o is NULL (lse may be NULL: then it is not written) */
+    ATTN_ERR_SHAPE = 2,        /* B, H, S_q or S_k < 1 */
+    ATTN_ERR_UNSUPPORTED = 3,  /* d not 64 or 128, or unknown dtype */
+    ATTN_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
+    ATTN_ERR_OVERFLOW = 5,     /* S*d or the grid size exceeds the 32-bit index range */
+    ATTN_ERR_VALUE = 6,        /* scale is not finite or not > 0 */
+    ATTN_ERR_LAUNCH = 7,       /* the HIP runtime refused the launch (no device, bad stream, ...) */
+    ATTN_ERR_DESCALE = 8       /* fp8 path: a descale pointer is NULL or misaligned (4 bytes) */
+} attn_status;
+
+/*
+ * Exact-attention forward for fp16 / bf16 (and unit-descale fp8) inputs.
+ *   q, k, v : device pointers, layout above, element type per `dtype`
+ *   o       : device pointer, [B][H][S_q][d]; f16 for ATTN_F16, bf16 otherwise
+ *   lse     : device pointer to [B][H][S_q] fp32, natural-log LSE; may be NULL
+ *   scale   : multiplies q.k before the softmax (finite, > 0), e.g. 1/sqrt(d)
+ *   causal  : 0 = all keys, otherwise key j visible to query i iff j <= i
+ *   stream  : hipStream_t or NULL
+ * Returns an attn_status.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S_q, int S_k,
+             int d, int causal, float scale, int dtype, void *stream);
+
+/*
+ * Exact-attention forward for block-scaled fp8 inputs (the FlashAttention-3
+ * deep dive, section 4: per-block scale factors from each block's local
+ * maximum; the score product in FP8, the softmax and the output accumulated
+ * in FP32).  q, k, v hold OCP E4M3 codes; the real value of element
+ * [b,h,r,t] is e4m3(code) * descale[b,h,r/128].
+ *   q_descale : fp32 [B][H][ceil(S_q/128)]
+ *   k_descale : fp32 [B][H][ceil(S_k/128)]
+ *   v_descale : fp32 [B][H][ceil(S_k/128)]
+ *   o         : bf16 [B][H][S_q][d]
+ * Other arguments as for attn_fwd.  Descales must be finite and > 0.
+ */
+int attn_fwd_fp8(const void *q, const void *k, const void *v, const float *q_descale, const float *k_descale,
+                 const float *v_descale, void *o, float *lse, int B, int H, int S_q, int S_k, int d, int causal,
+                 float scale, void *stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char *attn_status_string(int status);
+
+/*
+ * Tile shape the library launches for a problem (for reports and tests):
+ * writes queries per workgroup, keys per tile, waves per workgroup and the
+ * workgroup count.  Returns an attn_status (argument checks as attn_fwd, no
+ * device access).
+ */
+int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, int dtype, int *block_q, int *block_k,
+                  int *waves, int *workgroups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads, exports what include/attn.h declares, and rejects bad arguments on the host.
+
+No compute call is made here: every call below fails validation before the
+library touches the HIP runtime (the pointers are fake integers and are never
+dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_32_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, OVERFLOW, VALUE, LAUNCH, DESCALE = range(9)
+P = 0x10000   # a fake, 16-byte aligned "device pointer" (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ea.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_fwd_plan"}
+    for n in names:
+        assert hasattr(lib, n), f"library does not export {n}"
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = lib.attn_status_string(code)
+        assert s and s.decode() != "unknown status"
+    assert lib.attn_status_string(99).decode() == "unknown status"
+
+
+def call(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Sq=16, Sk=16, d=128, causal=0, scale=0.125, dtype=1):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, None)
+
+
+def call8(lib, q=P, k=P, v=P, qd=P, kd=P, vd=P, o=P, lse=P, B=1, H=1, Sq=16, Sk=16, d=128, causal=0, scale=0.125):
+    return lib.attn_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, H, Sq, Sk, d, causal, scale, None)
+
+
+def test_null_pointers(lib):
+    for kw in ("q", "k", "v", "o"):
+        assert call(lib, **{kw: None}) == NULL
+        assert call8(lib, **{kw: None}) == NULL
+    for kw in ("qd", "kd", "vd"):
+        assert call8(lib, **{kw: None}) == DESCALE
+
+
+def test_shapes(lib):
+    for kw in ("B", "H", "Sq", "Sk"):
+        assert call(lib, **{kw: 0}) == SHAPE
+        assert call(lib, **{kw: -3}) == SHAPE
+        assert call8(lib, **{kw: 0}) == SHAPE
+
+
+def test_unsupported(lib):
+    for d in (0, 32, 96, 256, 127):
+        assert call(lib, d=d) == UNSUP
+    assert call(lib, dtype=7) == UNSUP
+    assert call(lib, dtype=-1) == UNSUP
+
+
+def test_alignment(lib):
+    for kw in ("q", "k", "v", "o"):
+        assert call(lib, **{kw: P + 8}) == ALIGN
+        assert call8(lib, **{kw: P + 2}) == ALIGN
+    assert call(lib, lse=P + 2) == ALIGN
+    assert call8(lib, qd=P + 2) == DESCALE
+
+
+def test_overflow(lib):
+    assert call(lib, Sq=(2 ** 31 - 1) // 64, d=128) == OVERFLOW
+    assert call(lib, Sk=2 ** 25, d=64) == OVERFLOW
+    # grid size: ceil(S_q / block_q) * B * H must fit in an int
+    assert call(lib, B=2 ** 16, H=2 ** 16, Sq=16) == OVERFLOW
+
+
+def test_scale(lib):
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(lib, scale=s) == VALUE
+        assert call8(lib, scale=s) == VALUE
+
+
+def test_plan(lib):
+    bq, bk, w, n = ea.plan(2, 16, 4096, 4096, 128, False)
+    assert bq >= 32 and bq % 32 == 0 and bk % 32 == 0 and w >= 1
+    assert n == -(-4096 // bq) * 32
+    with pytest.raises(ea.AttnError):
+        ea.plan(1, 1, 16, 16, 96)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.fwd(q, q, q)

@@ -1,0 +1,135 @@
+"""GPU parity: the HIP kernels against the fp64 oracle, element by element.
+
+Gate (spec tolerances): max |O - O_ref| <= 1e-2 for f16/bf16 and 5e-2 for
+fp8, measured on top of each element's own output rounding
+(|round(O_ref) - O_ref|, which alone can exceed 1e-2 where |O| >= 4 in bf16);
+max |LSE - LSE_ref| <= 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_32_amd import inputs as I
+from oracle import attn_oracle
+from tests import parity_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_32_amd as ea
+
+    ea.load_library()
+    return attn_oracle.get()
+
+
+# (B, H, S_q, S_k, d): several tiles plus ragged tails, S_q != S_k, tiny and single-row cases
+SMALL = [
+    (1, 1, 1, 1, 64),
+    (1, 1, 1, 1, 128),
+    (1, 2, 3, 17, 128),
+    (1, 2, 17, 3, 64),
+    (1, 1, 17, 17, 128),
+    (2, 3, 130, 130, 64),
+    (1, 2, 130, 200, 128),
+    (2, 2, 300, 333, 128),
+    (1, 3, 333, 300, 64),
+    (1, 2, 513, 257, 128),
+    (2, 1, 640, 640, 64),
+    (1, 2, 1000, 1000, 128),
+]
+
+
+def _run_full(oracle, w):
+    x = I.make_inputs(w)
+    U.say(f"[gpu] {w.name} causal={w.causal}")
+    o, lse = U.run_gpu(x)
+    q, k, v = U.oracle_inputs(x, oracle)
+    ro, rl = oracle.attention(q, k, v, w.causal, w.scale)
+    st = U.compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, w.dtype)
+    U.say(f"   {st}")
+    return st
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_full(oracle, shape, dtype, causal):
+    B, H, Sq, Sk, d = shape
+    w = I.random_workload(B, H, Sq, Sk, d, dtype, causal, seed=1000 + Sq + 7 * Sk + d)
+    st = _run_full(oracle, w)
+    assert st["pass"], st
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_outliers_small(oracle, causal):
+    w = I.random_workload(1, 2, 700, 700, 64, "bf16", causal, seed=55, outliers=True)
+    st = _run_full(oracle, w)
+    assert st["pass"], st
+
+
+def test_tiny_workload_full(oracle):
+    w = I.WORKLOADS["f16_b1_h2_s128_d64"]
+    st = _run_full(oracle, w)
+    assert st["pass"], st
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_invariant_inputs(oracle, d, causal):
+    """V = 1 gives O = 1; Q = 0 gives the mean of the visible V rows and LSE = log(count)."""
+    dev = "cuda:0"
+    import exact_attention_32_amd as ea
+
+    B, H, S = 1, 2, 300
+    U.say(f"[gpu] invariants d={d} causal={causal}")
+    g = torch.Generator().manual_seed(d + causal)
+    q = torch.randn(B, H, S, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, S, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, S, d, generator=g).to(torch.bfloat16)
+    ones = torch.ones_like(v)
+    o, _ = ea.fwd(q.to(dev), k.to(dev), ones.to(dev), causal=causal, scale=d ** -0.5)
+    assert torch.all(o.cpu().float() == 1.0)
+    z = torch.zeros_like(q)
+    o, lse = ea.fwd(z.to(dev), k.to(dev), v.to(dev), causal=causal, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    vv = v.double()
+    n = torch.arange(1, S + 1, dtype=torch.float64)
+    ref = (vv.cumsum(2) / n[None, None, :, None]) if causal else vv.mean(2, keepdim=True).expand_as(vv)
+    ref_lse = torch.log(n) if causal else torch.full((S,), float(np.log(S)), dtype=torch.float64)
+    err = (o.cpu().double() - ref).abs()
+    floor = torch.from_numpy(U.rounding_floor(ref.numpy(), "bf16"))
+    assert float((err - floor).max()) <= 1e-2
+    assert float((lse.cpu().double() - ref_lse).abs().max()) <= 1e-3
+
+
+def test_deterministic(oracle):
+    w = I.random_workload(2, 4, 777, 777, 128, "bf16", True, seed=77)
+    x = I.make_inputs(w)
+    U.say(f"[gpu] determinism {w.name}")
+    o1, l1 = U.run_gpu(x)
+    o2, l2 = U.run_gpu(x)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", sorted(I.WORKLOADS))
+def test_workload_sampled_rows(oracle, name):
+    """Full-size workloads in the benchmark's launch configuration, checked on sampled rows."""
+    w = I.WORKLOADS[name]
+    x = I.make_inputs(w)
+    U.say(f"[gpu] {name}")
+    o, lse = U.run_gpu(x)
+    o = o.view(w.B * w.H, w.S_q, w.d)
+    lse = lse.view(w.B * w.H, w.S_q)
+    rows = U.sample_rows(w, n_random=200, seed=w.seed)
+    og = o[rows[:, 0], rows[:, 1]].double().cpu().numpy()
+    lg = lse[rows[:, 0], rows[:, 1]].double().cpu().numpy()
+    q, k, v = U.oracle_inputs(x, oracle)
+    ro, rl = oracle.attention_rows(q, k, v, w.causal, w.scale, rows)
+    st = U.compare(og, lg, ro, rl, w.dtype)
+    U.say(f"   {st}")
+    assert st["pass"], st
+    # properties at every row: finite outputs; LSE of a causal row i is >= log-free bound: LSE >= s_ii
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
