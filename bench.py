@@ -1,0 +1,228 @@
+"""Benchmark of the fused exact-attention forward on one MI355X.
+
+One step = one attention forward (one kernel launch) over the whole batch of
+the workload, inputs already resident in HBM.  Prints ONE JSON line:
+  value   : algorithmic TFLOP/s (4*d FLOP per visible (query, key) pair) over
+            exactly --steps launches, timed between device synchronisations;
+  roofline: the kernel's average launch duration from HIP events recorded on
+            the stream it is launched on, against MI355X dense MFMA peak
+            (bf16/fp16 2.5 PFLOP/s, fp8 5.0 PFLOP/s); `traffic` is the HBM
+            bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters
+            (profiles/*_pmc.txt) scaled by a copy-kernel calibration, reported
+            only while the kernel source is unchanged since the counters were
+            taken;
+  cpu_baseline: the fp64 CPU oracle timed on this host's cores on a bounded
+            sample of the same workload (whole heads), in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "bf16_b2_h16_s4096_d128"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_32_amd", "csrc", "attn_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch from the committed PMC summary, if taken on this kernel source."""
+    path = os.path.join(PROFILES, f"attn_fwd_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_sha():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def run_gpu(work, x, steps: int, warmup: int):
+    import torch
+
+    import exact_attention_32_amd as ea
+
+    dev = torch.device("cuda:0")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    o = torch.empty((work.B, work.H, work.S_q, work.d), device=dev,
+                    dtype=torch.float16 if work.dtype == "f16" else torch.bfloat16)
+    lse = torch.empty((work.B, work.H, work.S_q), device=dev, dtype=torch.float32)
+    if work.dtype == "fp8":
+        qd, kd, vd = x.q_descale.to(dev), x.k_descale.to(dev), x.v_descale.to(dev)
+
+        def step():
+            ea.fwd_fp8(q, k, v, qd, kd, vd, causal=work.causal, scale=work.scale, out=o, lse=lse)
+    else:
+        def step():
+            ea.fwd(q, k, v, causal=work.causal, scale=work.scale, out=o, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)   # the stream the kernel is launched on
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, per_launch_ms
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain device copy of MIB MiB (HBM counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); every (b, h) head is "
+              "independent, so sharding heads over GPUs needs no communication, but no multi-GPU path is built.",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    if args.copy_calibration > 0:
+        return copy_calibration(args.copy_calibration, max(1, args.steps))
+
+    import numpy as np
+
+    from exact_attention_32_amd import inputs as I
+
+    if args.workload not in I.WORKLOADS:
+        print(f"bench.py: unknown workload {args.workload}; choose from {sorted(I.WORKLOADS)}", file=sys.stderr)
+        return 2
+    work = I.WORKLOADS[args.workload]
+    x = I.make_inputs(work)
+
+    wall, per_launch = run_gpu(work, x, args.steps, args.warmup)
+    flops = work.flops()
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_launch_ms = float(np.mean(per_launch))
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[work.dtype]
+
+    result = {
+        "metric": "attention fwd TFLOP/s and % of MI355X peak MFMA (bf16, fp8)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": work.dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {"workload": work.name, "B": work.B, "H": work.H, "S_q": work.S_q, "S_k": work.S_k, "d": work.d,
+                   "causal": work.causal, "dtype": work.dtype, "scale": work.scale},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": counter_traffic(work.name),
+            "kernel": "attn_fwd_kernel",
+            "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+            "min_launch_us": round(float(np.min(per_launch)) * 1e3, 2),
+            "algorithmic_flop_per_launch": flops,
+            "algorithmic_hbm_bytes_per_launch": work.hbm_bytes(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = run_cpu_baseline(work, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def copy_calibration(mib: int, reps: int) -> int:
+    """A plain device-to-device copy of known size: what FETCH_SIZE / WRITE_SIZE read per byte moved."""
+    import torch
+
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": reps}), flush=True)
+    return 0
+
+
+def run_cpu_baseline(work, x, target_s: float):
+    """The fp64 oracle on whole (b, h) heads of the same workload, sized to about target_s seconds."""
+    import numpy as np
+
+    from oracle import attn_oracle
+
+    orc = attn_oracle.get()
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    BH = work.B * work.H
+
+    qa, ka, va = _oracle_arrays(work, x, orc)
+
+    def timed(n):
+        q = np.ascontiguousarray(qa.reshape(BH, *qa.shape[2:])[:n][None])
+        k = np.ascontiguousarray(ka.reshape(BH, *ka.shape[2:])[:n][None])
+        v = np.ascontiguousarray(va.reshape(BH, *va.shape[2:])[:n][None])
+        t0 = time.perf_counter()
+        orc.attention(q, k, v, work.causal, work.scale, nthreads=threads)
+        return time.perf_counter() - t0
+
+    t1 = timed(1)
+    n = int(min(BH, max(1, round(target_s / max(t1, 1e-6)))))
+    t = timed(n) if n > 1 else t1
+    flops = work.flops() * n // BH
+    used = orc.last_threads
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": f"{n} of {BH} (b,h) heads of {work.name}, all {work.S_q} query rows each, fp64 explicit "
+                      f"softmax; {t:.2f} s on {used} threads"}
+
+
+def _oracle_arrays(work, x, orc):
+    if work.dtype == "fp8":
+        return (orc.decode_e4m3_blocks(x.q.numpy(), x.q_descale.numpy()),
+                orc.decode_e4m3_blocks(x.k.numpy(), x.k_descale.numpy()),
+                orc.decode_e4m3_blocks(x.v.numpy(), x.v_descale.numpy()))
+    return x.q.double().numpy(), x.k.double().numpy(), x.v.double().numpy()
+
+
+if __name__ == "__main__":
+    sys.exit(main())

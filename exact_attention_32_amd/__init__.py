@@ -24,9 +24,10 @@ class AttnError(RuntimeError):
     pass
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+def load_library(path: str | None = None) -> ctypes.CDLL:
     """Load the HIP library (raises if it has not been built)."""
     global _lib
+    path = path or LIB_PATH
     if _lib is not None and path == LIB_PATH:
         return _lib
     if not os.path.exists(path):

@@ -17,6 +17,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around the softmax rescale)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

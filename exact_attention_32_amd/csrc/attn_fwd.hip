@@ -43,16 +43,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// clang vector types (not HIP's u32x4 struct, whose copies go through memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct BF16 {};
 struct F16 {};
 
-template <class T> __device__ __forceinline__ f32x16 mfma_32x32x16(uint4 a, uint4 b, f32x16 c);
-template <> __device__ __forceinline__ f32x16 mfma_32x32x16<BF16>(uint4 a, uint4 b, f32x16 c) {
+template <class T> __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 mfma_32x32x16<BF16>(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
 }
-template <> __device__ __forceinline__ f32x16 mfma_32x32x16<F16>(uint4 a, uint4 b, f32x16 c) {
+template <> __device__ __forceinline__ f32x16 mfma_32x32x16<F16>(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                   0, 0);
 }
@@ -93,6 +96,9 @@ struct Params {
 // 16 keys, keys 4..7 and 8..11 trade places, so that the 8 keys lane half g
 // feeds to one 32x32x16 MFMA step (keys 4g..4g+3 and 8+4g..8+4g+3 of the
 // accumulator layout) are contiguous.
+// Dword i (compile-time after unrolling) of a 16-byte register group.
+__device__ __forceinline__ uint32_t word(u32x4 v, int i) { return v[i]; }
+
 __device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 template <class T, int D, int QB, int NW, int BC, bool CAUSAL>
@@ -104,10 +110,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     constexpr int KBUF = BC * KSTR;
     constexpr int VBUF = D * VSTR;
     constexpr int KCHUNKS = BC * D / 8;        // 16-byte chunks in a K tile
-    constexpr int KPT = (KCHUNKS + NT - 1) / NT;
+    constexpr int KPT = KCHUNKS / NT;
     constexpr int VTASKS = (D / 8) * (BC / 4); // 4 keys x 8 columns per task
-    constexpr int VPT = (VTASKS + NT - 1) / NT;
+    constexpr int VPT = VTASKS / NT;
     static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(KCHUNKS % NT == 0 && VTASKS % NT == 0 && KPT >= 1 && VPT >= 1, "tile loads must split evenly");
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (KBUF + VBUF)];
 
     const int tid = threadIdx.x;
@@ -129,17 +136,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const int qw0 = q0 + wave * QB * 32;   // first query of this wave
 
     // Q^T operands, resident for the whole key loop.
-    uint4 qf[QB][D / 16];
+    u32x4 qf[QB][D / 16];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int row = qw0 + qb * 32 + l32;
+        const int row = min(qw0 + qb * 32 + l32, Sq - 1);   // rows past S_q are computed, never stored
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            if (row < Sq)
-                qf[qb][ks] = *reinterpret_cast<const uint4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
-            else
-                qf[qb][ks] = make_uint4(0, 0, 0, 0);
-        }
+        for (int ks = 0; ks < D / 16; ++ks)
+            qf[qb][ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
     }
 
     f32x16 oacc[QB][D / 32];
@@ -160,67 +163,65 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         nt = min(nt, qlast / BC + 1);
     }
 
-    uint4 kst[KPT];
-    uint4 vst[VPT][4];
+    u32x4 kst[KPT];
+    u32x4 vst[VPT][4];
 
-    auto load_tile = [&](int t) {
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BC;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int c = tid + j * NT;
-            if (c < KCHUNKS) {
+            {
                 const int r = c / (D / 8), col = c % (D / 8);
-                if (k0 + r < Sk)
-                    kst[j] = *reinterpret_cast<const uint4 *>(Kh + (size_t)(k0 + r) * D + col * 8);
-                else
-                    kst[j] = make_uint4(0, 0, 0, 0);
+                // rows past S_k are clamped onto the last key: their scores are masked to -inf
+                // and their P is exactly 0, so any finite value is harmless
+                const int key = min(k0 + r, Sk - 1);
+                kst[j] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)key * D + col * 8);
             }
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int tk = tid + j * NT;
-            if (tk < VTASKS) {
-                const int cg = tk % (D / 8), rg = tk / (D / 8);
+            {
+                const int rg = tk % (BC / 4), cg = tk / (BC / 4);   // key groups across lanes: conflict-free V^T writes
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int key = k0 + rg * 4 + r;
-                    if (key < Sk)
-                        vst[j][r] = *reinterpret_cast<const uint4 *>(Vh + (size_t)key * D + cg * 8);
-                    else
-                        vst[j][r] = make_uint4(0, 0, 0, 0);
+                    const int key = min(k0 + rg * 4 + r, Sk - 1);
+                    vst[j][r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)key * D + cg * 8);
                 }
             }
         }
     };
 
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
         unsigned char *kb = smem + buf * (KBUF + VBUF);
         unsigned char *vb = kb + KBUF;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int c = tid + j * NT;
-            if (c < KCHUNKS) {
+            {
                 const int r = c / (D / 8), col = c % (D / 8);
-                *reinterpret_cast<uint4 *>(kb + r * KSTR + col * 16) = kst[j];
+                *reinterpret_cast<u32x4 *>(kb + r * KSTR + col * 16) = kst[j];
             }
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int tk = tid + j * NT;
-            if (tk < VTASKS) {
-                const int cg = tk % (D / 8), rg = tk / (D / 8);
+            {
+                const int rg = tk % (BC / 4), cg = tk / (BC / 4);   // key groups across lanes: conflict-free V^T writes
                 const int pos = vt_pos(rg * 4);
-                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&vst[j][0]);
-                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&vst[j][1]);
-                const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&vst[j][2]);
-                const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&vst[j][3]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int sh = (e & 1) * 16;
-                    const uint32_t a0 = (w0[e >> 1] >> sh) & 0xffffu, a1 = (w1[e >> 1] >> sh) & 0xffffu;
-                    const uint32_t a2 = (w2[e >> 1] >> sh) & 0xffffu, a3 = (w3[e >> 1] >> sh) & 0xffffu;
-                    uint2 val = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-                    *reinterpret_cast<uint2 *>(vb + (cg * 8 + e) * VSTR + pos * 2) = val;
+                    // column e of the 4 staged rows -> 4 consecutive keys of V^T row (cg*8 + e)
+                    const uint32_t w0 = word(vst[j][0], e >> 1), w1 = word(vst[j][1], e >> 1);
+                    const uint32_t w2 = word(vst[j][2], e >> 1), w3 = word(vst[j][3], e >> 1);
+                    u32x2 val;
+                    if (e & 1) {
+                        val = u32x2{(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
+                    } else {
+                        val = u32x2{(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+                    }
+                    *reinterpret_cast<u32x2 *>(vb + (cg * 8 + e) * VSTR + pos * 2) = val;
                 }
             }
         }
@@ -228,6 +229,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 
     load_tile(0);
     store_tile(0);
+    // Drain every outstanding load (the Q fragments included) before the key loop: the memory
+    // counter is in order, so a first wait on Q inside the loop would also wait on the
+    // prefetch of the next K/V tile.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     const float c = p.c;
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
             for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
-                    const uint4 a = *reinterpret_cast<const uint4 *>(kb + (kb2 * 32 + l32) * KSTR + ks * 32 + g * 16);
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + (kb2 * 32 + l32) * KSTR + ks * 32 + g * 16);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) s[qb][kb2] = mfma_32x32x16<T>(a, qf[qb][ks], s[qb][kb2]);
                 }
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                 }
             }
             // online softmax (base 2), P packed to T as the B operand of P.V
-            uint4 pf[QB][BC / 16];
+            u32x4 pf[QB][BC / 16];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 float mx = -INFINITY;
@@ -281,33 +286,41 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb2][i]);
                 mx = xhalf_max(mx) * c;
-                const float mnew = fmaxf(mrow[qb], mx);
-                const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
-                const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - mbase);
-                mrow[qb] = mnew;
-                float ls = 0.f;
+                // O and l are rescaled only when some row of the wave raises its max (wave-uniform
+                // branch; rows whose max did not move get alpha = 1).
+                if (__builtin_amdgcn_ballot_w64(mx > mrow[qb]) != 0) {
+                    const float mnew = fmaxf(mrow[qb], mx);
+                    const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - (mnew == -INFINITY ? 0.f : mnew));
+                    mrow[qb] = mnew;
+                    lrow[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+                }
+                const float mbase = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
 #pragma unroll
                 for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][i], c, -mbase));
-                        s[qb][kb2][i] = pv;
-                        ls += pv;
-                    }
-                lrow[qb] = lrow[qb] * alpha + ls;
+                    for (int i = 0; i < 16; ++i)
+                        s[qb][kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][i], c, -mbase));
+                // l: fp32 sum of p.  The running max is exact, so the largest p of a row is exactly 1
+                // and survives the rounding of P to T unchanged.
+                float ls = lrow[qb];
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+                for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+                    for (int i = 0; i < 16; ++i) ls += s[qb][kb2][i];
+                lrow[qb] = ls;
 #pragma unroll
                 for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int o = h * 8;
-                        pf[qb][kb2 * 2 + h] = make_uint4(pack2<T>(s[qb][kb2][o + 0], s[qb][kb2][o + 1]),
-                                                         pack2<T>(s[qb][kb2][o + 2], s[qb][kb2][o + 3]),
-                                                         pack2<T>(s[qb][kb2][o + 4], s[qb][kb2][o + 5]),
-                                                         pack2<T>(s[qb][kb2][o + 6], s[qb][kb2][o + 7]));
+                        pf[qb][kb2 * 2 + h] = u32x4{pack2<T>(s[qb][kb2][o + 0], s[qb][kb2][o + 1]),
+                                                    pack2<T>(s[qb][kb2][o + 2], s[qb][kb2][o + 3]),
+                                                    pack2<T>(s[qb][kb2][o + 4], s[qb][kb2][o + 5]),
+                                                    pack2<T>(s[qb][kb2][o + 6], s[qb][kb2][o + 7])};
                     }
             }
             // O^T += V^T P^T
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
             for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const uint4 a = *reinterpret_cast<const uint4 *>(vb + (db * 32 + l32) * VSTR + ks * 32 + g * 16);
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(vb + (db * 32 + l32) * VSTR + ks * 32 + g * 16);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_32x32x16<T>(a, pf[qb][ks], oacc[qb][db]);
                 }
@@ -338,9 +351,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 #pragma unroll
                 for (int gi = 0; gi < 4; ++gi) {
                     const int dv = db * 32 + 8 * gi + 4 * g;
-                    uint2 val = make_uint2(pack2<T>(oacc[qb][db][gi * 4 + 0] * inv, oacc[qb][db][gi * 4 + 1] * inv),
-                                           pack2<T>(oacc[qb][db][gi * 4 + 2] * inv, oacc[qb][db][gi * 4 + 3] * inv));
-                    *reinterpret_cast<uint2 *>(orow + dv) = val;
+                    u32x2 val = u32x2{pack2<T>(oacc[qb][db][gi * 4 + 0] * inv, oacc[qb][db][gi * 4 + 1] * inv),
+                                           pack2<T>(oacc[qb][db][gi * 4 + 2] * inv, oacc[qb][db][gi * 4 + 3] * inv)};
+                    *reinterpret_cast<u32x2 *>(orow + dv) = val;
                 }
             if (p.lse && g == 0) p.lse[(size_t)bh * Sq + qrow] = (mrow[qb] + log2f(lt)) * 0.69314718055994530942f;
         }

@@ -33,6 +33,15 @@ def build(src: str = SRC, out: str = LIB) -> str:
 _dptr = ctypes.POINTER(ctypes.c_double)
 
 
+def default_threads() -> int:
+    """Worker threads for the oracle: this process's CPUs, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _p(a: np.ndarray):
     return a.ctypes.data_as(_dptr)
 
@@ -83,7 +92,7 @@ class Oracle:
         o = np.empty((B, H, Sq, d), np.float64)
         lse = np.empty((B, H, Sq), np.float64)
         n = self.L.oracle_attn_explicit(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Sq, Sk, d, int(causal),
-                                        float(scale), int(nthreads))
+                                        float(scale), int(nthreads) if nthreads > 0 else default_threads())
         if n < 0:
             raise ValueError("oracle rejected arguments")
         self.last_threads = n
@@ -96,7 +105,7 @@ class Oracle:
         o = np.empty((B, H, Sq, d), np.float64)
         lse = np.empty((B, H, Sq), np.float64)
         n = self.L.oracle_attn_online(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Sq, Sk, d, int(causal),
-                                      float(scale), int(bc), int(nthreads))
+                                      float(scale), int(bc), int(nthreads) if nthreads > 0 else default_threads())
         if n < 0:
             raise ValueError("oracle rejected arguments")
         self.last_threads = n
@@ -111,7 +120,7 @@ class Oracle:
         o = np.empty((n, d), np.float64)
         lse = np.empty((n,), np.float64)
         r = self.L.oracle_attn_rows(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Sq, Sk, d, int(causal),
-                                    float(scale), rows.ctypes.data, n, int(nthreads))
+                                    float(scale), rows.ctypes.data, n, int(nthreads) if nthreads > 0 else default_threads())
         if r < 0:
             raise ValueError("oracle rejected arguments")
         self.last_threads = r
