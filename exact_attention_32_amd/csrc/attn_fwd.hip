@@ -32,7 +32,11 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -71,6 +75,27 @@ template <> __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + a.lo + a.hi for a dword holding two 16-bit values of type T (one v_dot2 against ones).
+template <class T> __device__ __forceinline__ float sum2(uint32_t a, float acc);
+template <> __device__ __forceinline__ float sum2<BF16>(uint32_t a, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), one, acc, false);
+}
+template <> __device__ __forceinline__ float sum2<F16>(uint32_t a, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), one, acc, false);
+}
+
+#ifndef ATTN_LAZY
+#define ATTN_LAZY 1
+#endif
+#ifndef ATTN_PRIO
+#define ATTN_PRIO 0
+#endif
+// The running max moves only when a row's max would grow by more than RESCALE_LOG2 (base 2);
+// until then p = exp2(s*c - m) <= 2^RESCALE_LOG2 and the O rescale is skipped.
+constexpr float RESCALE_LOG2 = ATTN_LAZY ? 8.0f : 0.0f;
+
 // Row max between lane l and lane l^32 (the two halves of a 32x32 accumulator column).
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -92,33 +117,107 @@ struct Params {
     float c;         // scale * log2(e)
 };
 
-// Position of key r (0 <= r < BC) in a transposed V row: within each group of
-// 16 keys, keys 4..7 and 8..11 trade places, so that the 8 keys lane half g
-// feeds to one 32x32x16 MFMA step (keys 4g..4g+3 and 8+4g..8+4g+3 of the
-// accumulator layout) are contiguous.
-// Dword i (compile-time after unrolling) of a 16-byte register group.
-__device__ __forceinline__ uint32_t word(u32x4 v, int i) { return v[i]; }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// K and V tiles sit in LDS row-major (one key per row, 2*D bytes, no padding).  The 16-byte
+// chunk c of row r is stored at chunk position c ^ swz(r): the XOR spreads the rows read by
+// one MFMA operand fetch over all LDS banks, both for the K fetch (32 consecutive rows, one
+// chunk each) and for the transposed V fetch (8 rows, 4 consecutive chunks each).
+template <int D> __device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
-template <class T, int D, int QB, int NW, int BC, bool CAUSAL>
+// Wait until at most N of this wave's vector-memory loads are outstanding (they complete in
+// order): s_waitcnt with the vmcnt field (bits 3:0 and 15:14) set to N and the expcnt and
+// lgkmcnt fields at "no wait".
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence (a fence would drain the in-flight direct-to-LDS
+// loads of later tiles).  The LDS data a wave needs is covered by its explicit memory-counter
+// wait before the barrier; the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int I, int N, class F> __device__ __forceinline__ void static_for_impl(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_impl<I + 1, N>(f);
+    }
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F &&f) { static_for_impl<0, N>(f); }
+
+// Instruction-scheduling hint for a block of NSTEP k-steps, each READS_PER LDS reads feeding
+// MFMA_PER MFMAs: PRE reads first, then alternately the MFMAs of one step and the reads of a
+// later one, so that LDS latency overlaps the matrix core instead of stalling every MFMA.
+template <int PRE, int READS_PER, int MFMA_PER, int NSTEP>
+__device__ __forceinline__ void sched_reads_ahead() {
+    constexpr int DS_READ = 0x100, MFMA = 0x008;
+    __builtin_amdgcn_sched_group_barrier(DS_READ, PRE, 0);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, MFMA_PER, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_READ, READS_PER, 0);
+    }
+}
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane j receives element (j % 4) of the
+// 8-byte words addressed by lanes 4k + j/4, for k = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char *ptr) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(ptr));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address lds + 16 l.
+// Written as asm so that the compiler's own memory-counter bookkeeping does not see it (it
+// would otherwise wait for these loads before any later LDS read it cannot tell apart); every
+// wait for them is explicit.  The address registers are read when the load issues.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
+    return (uint32_t)(uintptr_t)(const lds_u8 *)p;
+}
+
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+// LDS reads at a 32-bit LDS byte address; OFF is a compile-time offset that the instruction's
+// immediate field absorbs
+template <int OFF> __device__ __forceinline__ u32x4 lds_load_b128(uint32_t addr) {
+    return *(const lds_u32x4 *)(uintptr_t)(addr + OFF);
+}
+template <int OFF> __device__ __forceinline__ u32x2 lds_load_tr16(uint32_t addr) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(addr + OFF));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <class T, int D, int QB, int NW, int BC, int NS, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
-    constexpr int NT = NW * 64;                // threads
-    constexpr int BR = NW * QB * 32;           // queries per workgroup
-    constexpr int KSTR = D * 2 + 16;           // bytes per K row in LDS (padded)
-    constexpr int VSTR = BC * 2 + 16;          // bytes per V^T row in LDS (padded)
-    constexpr int KBUF = BC * KSTR;
-    constexpr int VBUF = D * VSTR;
-    constexpr int KCHUNKS = BC * D / 8;        // 16-byte chunks in a K tile
-    constexpr int KPT = KCHUNKS / NT;
-    constexpr int VTASKS = (D / 8) * (BC / 4); // 4 keys x 8 columns per task
-    constexpr int VPT = VTASKS / NT;
-    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert(KCHUNKS % NT == 0 && VTASKS % NT == 0 && KPT >= 1 && VPT >= 1, "tile loads must split evenly");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * (KBUF + VBUF)];
+    constexpr int BR = NW * QB * 32;     // queries per workgroup
+    constexpr int ROWB = 2 * D;          // bytes per K/V row in LDS
+    constexpr int TILEB = BC * ROWB;     // bytes per K (or V) tile
+    constexpr int NBLK = TILEB / 1024;   // 1 KiB direct-to-LDS blocks per tile
+    constexpr int BPW = NBLK / NW;       // blocks per wave
+    static_assert(BC % 32 == 0 && D % 32 == 0 && NBLK % NW == 0 && BPW >= 1, "tile shape");
+    // NS stages: tile t is read while tiles t+1 .. t+NS-2 are in flight
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS][2][TILEB];   // [stage][K, V]
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
 
     int L = blockIdx.x;
@@ -135,214 +234,225 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 
     const int qw0 = q0 + wave * QB * 32;   // first query of this wave
 
-    // Q^T operands, resident for the whole key loop.
-    u32x4 qf[QB][D / 16];
+    u32x4 qf[QB][D / 16];   // Q^T operands, loaded after the first K/V loads are issued
+
+    // per-lane LDS offsets of the MFMA operand fetches (the swizzle only sees row bits 0..3)
+    int koff[D / 16];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = min(qw0 + qb * 32 + l32, Sq - 1);   // rows past S_q are computed, never stored
+    for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + g) ^ swz<D>(l32)) << 4);
+    int voff[2][D / 32];
+    {
+        const int i = lane & 15, g2 = (lane >> 4) & 1;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            qf[qb][ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
+        for (int h = 0; h < 2; ++h) {
+            const int r = h * 8 + 4 * g + (i >> 2);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const int dv = db * 32 + 16 * g2 + 4 * (i & 3);
+                voff[h][db] = r * ROWB + (((dv >> 3) ^ swz<D>(r)) << 4) + ((dv >> 2) & 1) * 8;
+            }
+        }
+    }
+    // direct-to-LDS loads: block b of a tile is LDS bytes [1024 b, 1024 b + 1024); lane l fills
+    // 16 bytes at 1024 b + 16 l, i.e. row `grow`, chunk position `pch`, with global chunk
+    // pch ^ swz(row)
+    int grow[BPW], gcol[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int off = (wave * BPW + j) * 1024 + lane * 16;
+        grow[j] = off / ROWB;
+        gcol[j] = ((off % ROWB) >> 4 ^ swz<D>(grow[j])) * 8;
     }
 
     f32x16 oacc[QB][D / 32];
-    float mrow[QB], lrow[QB];
+    float mrow[QB], lrow[QB], lrnd[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         mrow[qb] = -INFINITY;
         lrow[qb] = 0.f;
+        lrnd[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
     }
 
-    int nt = (Sk + BC - 1) / BC;
+    // tiles [0, n_full) need no mask; [n_full, n_total) hold the causal diagonal or the S_k tail
+    int n_total = (Sk + BC - 1) / BC;
+    int n_full = Sk / BC;
     if (CAUSAL) {
-        const int qlast = min(q0 + BR, Sq) - 1;
-        nt = min(nt, qlast / BC + 1);
+        n_total = min(n_total, (min(q0 + BR, Sq) - 1) / BC + 1);
+        n_full = min(n_full, (q0 + 1) / BC);
     }
+    n_full = min(n_full, n_total);
 
-    u32x4 kst[KPT];
-    u32x4 vst[VPT][4];
-
-    auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const uint32_t smem0 = lds_addr(&smem[0][0][0]);
+    auto dma = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BC;
+        const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const int c = tid + j * NT;
-            {
-                const int r = c / (D / 8), col = c % (D / 8);
-                // rows past S_k are clamped onto the last key: their scores are masked to -inf
-                // and their P is exactly 0, so any finite value is harmless
-                const int key = min(k0 + r, Sk - 1);
-                kst[j] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)key * D + col * 8);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int tk = tid + j * NT;
-            {
-                const int rg = tk % (BC / 4), cg = tk / (BC / 4);   // key groups across lanes: conflict-free V^T writes
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = min(k0 + rg * 4 + r, Sk - 1);
-                    vst[j][r] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)key * D + cg * 8);
-                }
-            }
+        for (int j = 0; j < BPW; ++j) {
+            // rows past S_k are clamped onto the last key: their scores are masked to -inf and
+            // their P is exactly 0, so any finite value is harmless
+            const size_t e = (size_t)min(k0 + grow[j], Sk - 1) * D + gcol[j];
+            const uint32_t off = (uint32_t)((wave * BPW + j) * 1024);
+            dma16(Kh + e, st + off);
+            dma16(Vh + e, st + TILEB + off);
         }
     };
-
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
-        unsigned char *kb = smem + buf * (KBUF + VBUF);
-        unsigned char *vb = kb + KBUF;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const int c = tid + j * NT;
-            {
-                const int r = c / (D / 8), col = c % (D / 8);
-                *reinterpret_cast<u32x4 *>(kb + r * KSTR + col * 16) = kst[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int tk = tid + j * NT;
-            {
-                const int rg = tk % (BC / 4), cg = tk / (BC / 4);   // key groups across lanes: conflict-free V^T writes
-                const int pos = vt_pos(rg * 4);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // column e of the 4 staged rows -> 4 consecutive keys of V^T row (cg*8 + e)
-                    const uint32_t w0 = word(vst[j][0], e >> 1), w1 = word(vst[j][1], e >> 1);
-                    const uint32_t w2 = word(vst[j][2], e >> 1), w3 = word(vst[j][3], e >> 1);
-                    u32x2 val;
-                    if (e & 1) {
-                        val = u32x2{(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-                    } else {
-                        val = u32x2{(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-                    }
-                    *reinterpret_cast<u32x2 *>(vb + (cg * 8 + e) * VSTR + pos * 2) = val;
-                }
-            }
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    // Drain every outstanding load (the Q fragments included) before the key loop: the memory
-    // counter is in order, so a first wait on Q inside the loop would also wait on the
-    // prefetch of the next K/V tile.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     const float c = p.c;
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nt) load_tile(t + 1);
+    auto compute = [&](int t, const unsigned char *kb, const unsigned char *vb, bool masked)
+                       __attribute__((always_inline)) {
         const int k0 = t * BC;
-        const unsigned char *kb = smem + buf * (KBUF + VBUF);
-        const unsigned char *vb = kb + KBUF;
-        const bool active = !CAUSAL || k0 <= qw0 + QB * 32 - 1;
-        if (active) {
-            // S^T = K Q^T for this tile
-            f32x16 s[QB][BC / 32];
+        // S^T = K Q^T
+        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
+        f32x16 s[QB][BC / 32];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) s[qb][kb2][i] = 0.f;
+                for (int i = 0; i < 16; ++i) s[qb][kb2][i] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
+        for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
-                for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + (kb2 * 32 + l32) * KSTR + ks * 32 + g * 16);
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + kb2 * 32 * ROWB + koff[ks]);
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[qb][kb2] = mfma_32x32x16<T>(a, qf[qb][ks], s[qb][kb2]);
-                }
+                for (int qb = 0; qb < QB; ++qb) s[qb][kb2] = mfma_32x32x16<T>(a, qf[qb][ks], s[qb][kb2]);
             }
-            // mask: keys past S_k, and (causal) keys after the query
-            const bool need_mask = (k0 + BC > Sk) || (CAUSAL && k0 + BC - 1 > qw0);
-            if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int qrow = qw0 + qb * 32 + l32;
-#pragma unroll
-                    for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int key = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                            if (key >= Sk || (CAUSAL && key > qrow)) s[qb][kb2][i] = -INFINITY;
-                        }
-                }
-            }
-            // online softmax (base 2), P packed to T as the B operand of P.V
-            u32x4 pf[QB][BC / 16];
+        }
+        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+        if (masked) {
+            // element i of block kb2 holds key k0 + 4g + c with c = 32 kb2 + 8 (i / 4) + i % 4 (a
+            // constant); it is visible iff c < lim
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb2][i]);
-                mx = xhalf_max(mx) * c;
-                // O and l are rescaled only when some row of the wave raises its max (wave-uniform
-                // branch; rows whose max did not move get alpha = 1).
-                if (__builtin_amdgcn_ballot_w64(mx > mrow[qb]) != 0) {
-                    const float mnew = fmaxf(mrow[qb], mx);
-                    const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - (mnew == -INFINITY ? 0.f : mnew));
-                    mrow[qb] = mnew;
-                    lrow[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
-                }
-                const float mbase = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
+                const int base = k0 + 4 * g;
+                int lim = Sk - base;
+                if (CAUSAL) lim = min(lim, qw0 + qb * 32 + l32 + 1 - base);
 #pragma unroll
                 for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        s[qb][kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][i], c, -mbase));
-                // l: fp32 sum of p.  The running max is exact, so the largest p of a row is exactly 1
-                // and survives the rounding of P to T unchanged.
-                float ls = lrow[qb];
-#pragma unroll
-                for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) ls += s[qb][kb2][i];
-                lrow[qb] = ls;
-#pragma unroll
-                for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int o = h * 8;
-                        pf[qb][kb2 * 2 + h] = u32x4{pack2<T>(s[qb][kb2][o + 0], s[qb][kb2][o + 1]),
-                                                    pack2<T>(s[qb][kb2][o + 2], s[qb][kb2][o + 3]),
-                                                    pack2<T>(s[qb][kb2][o + 4], s[qb][kb2][o + 5]),
-                                                    pack2<T>(s[qb][kb2][o + 6], s[qb][kb2][o + 7])};
-                    }
-            }
-            // O^T += V^T P^T
-#pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks) {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(vb + (db * 32 + l32) * VSTR + ks * 32 + g * 16);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_32x32x16<T>(a, pf[qb][ks], oacc[qb][db]);
-                }
+                        if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[qb][kb2][i] = -INFINITY;
             }
         }
-        if (t + 1 < nt) store_tile(buf ^ 1);
-        __syncthreads();
+        // online softmax (base 2); P rounded to T is the B operand of P.V
+        u32x4 pf[QB][BC / 16];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb2][i]);
+            mx = xhalf_max(mx) * c;
+            // O and the row sums are rescaled only when some row of the wave raises its max by
+            // more than RESCALE_LOG2 (wave-uniform branch; other rows get alpha = 1)
+            if (__builtin_amdgcn_ballot_w64(mx > mrow[qb] + RESCALE_LOG2) != 0) {
+                const float mnew = fmaxf(mrow[qb], mx);
+                const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - (mnew == -INFINITY ? 0.f : mnew));
+                mrow[qb] = mnew;
+                lrow[qb] *= alpha;
+                lrnd[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+            }
+            const float mbase = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s[qb][kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][i], c, -mbase));
+            // lrow: fp32 sum of p, for the LSE.  lrnd: sum of p rounded to T (the values P.V
+            // uses), for the normalisation of O: with a stale max the largest p of a row is not
+            // 1, and its rounding cancels only if numerator and denominator see the same value.
+            float ls = lrow[qb], lr = lrnd[qb];
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ls += s[qb][kb2][i];
+            lrow[qb] = ls;
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int o = h * 8;
+                    const u32x4 pk = u32x4{pack2<T>(s[qb][kb2][o + 0], s[qb][kb2][o + 1]),
+                                           pack2<T>(s[qb][kb2][o + 2], s[qb][kb2][o + 3]),
+                                           pack2<T>(s[qb][kb2][o + 4], s[qb][kb2][o + 5]),
+                                           pack2<T>(s[qb][kb2][o + 6], s[qb][kb2][o + 7])};
+                    pf[qb][kb2 * 2 + h] = pk;
+                    if (ATTN_LAZY) lr = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr))));
+                }
+            lrnd[qb] = lr;
+        }
+        // O^T += V^T P^T; V^T is fetched with two transposing LDS reads per operand
+        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const u32x2 lo = lds_read_tr16(vb + ks * 16 * ROWB + voff[0][db]);
+                const u32x2 hi = lds_read_tr16(vb + ks * 16 * ROWB + voff[1][db]);
+                const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_32x32x16<T>(a, pf[qb][ks], oacc[qb][db]);
+            }
+        }
+        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
+    constexpr int LPT = 2 * BPW;   // direct-to-LDS loads per tile per wave
+
+    // one tile: wait until tile t is in LDS for every wave (this wave's loads of the next tiles
+    // may still be in flight), which also means every wave is done with tile t-1, whose stage
+    // then receives tile t+NS-1; compute on tile t
+    auto step = [&](int t, bool masked) __attribute__((always_inline)) {
+        const int ahead = min(NS - 2, n_total - 1 - t);   // tiles issued after t
+        if (NS >= 4 && ahead >= 2)
+            wait_vmcnt<2 * LPT>();
+        else if (NS >= 3 && ahead >= 1)
+            wait_vmcnt<LPT>();
+        else
+            wait_vmcnt<0>();
+        wg_barrier();
+        if (t + NS - 1 < n_total) dma(t + NS - 1);
+        // causal: a wave whose queries all precede the tile has nothing to add
+        if (!masked || !CAUSAL || t * BC <= qw0 + QB * 32 - 1)
+            compute(t, &smem[t % NS][0][0], &smem[t % NS][1][0], masked);
+    };
+
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+        if (u < n_total) dma(u);
+    // Q^T operands (B of the S^T MFMA), resident for the whole key loop.  Rows past S_q are
+    // clamped: they are computed and never stored.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = min(qw0 + qb * 32 + l32, Sq - 1);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qf[qb][ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
     }
+
+    // the Q fragments are the newest loads; draining them here keeps the in-order memory
+    // counter free of them inside the key loop
+    __builtin_amdgcn_s_waitcnt(0);
+
+    int t = 0;
+    for (; t < n_full; ++t) step(t, false);
+    for (; t < n_total; ++t) step(t, true);
 
     // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float lt = xhalf_sum(lrow[qb]);
-        const float inv = 1.0f / lt;
+        const float inv = 1.0f / (ATTN_LAZY ? xhalf_sum(lrnd[qb]) : lt);
         const int qrow = qw0 + qb * 32 + l32;
         if (qrow < Sq) {
             uint16_t *orow = p.o + ((size_t)bh * Sq + qrow) * D;
@@ -352,7 +462,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                 for (int gi = 0; gi < 4; ++gi) {
                     const int dv = db * 32 + 8 * gi + 4 * g;
                     u32x2 val = u32x2{pack2<T>(oacc[qb][db][gi * 4 + 0] * inv, oacc[qb][db][gi * 4 + 1] * inv),
-                                           pack2<T>(oacc[qb][db][gi * 4 + 2] * inv, oacc[qb][db][gi * 4 + 3] * inv)};
+                                      pack2<T>(oacc[qb][db][gi * 4 + 2] * inv, oacc[qb][db][gi * 4 + 3] * inv)};
                     *reinterpret_cast<u32x2 *>(orow + dv) = val;
                 }
             if (p.lse && g == 0) p.lse[(size_t)bh * Sq + qrow] = (mrow[qb] + log2f(lt)) * 0.69314718055994530942f;
@@ -360,11 +470,335 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     }
 }
 
+// Ping-pong schedule for two waves per SIMD.  Eight waves per workgroup, 32 queries each; the
+// waves are split into group A (waves 0-3) and group B (waves 4-7); wave w and wave w+4 share a
+// SIMD.  The key loop runs in barrier-separated intervals.  In its MFMA interval a wave does
+// O^T += V^T P^T for tile t-1 and S^T = K Q^T for tile t; in its VALU interval it runs the online
+// softmax of tile t.  Group B runs one interval behind group A, so in every interval one wave of
+// each SIMD keeps the matrix core busy while the other one does the softmax: the overlap of
+// GEMM and softmax that the FlashAttention-3 deep dive (techknowgenie), sections 2 and 3,
+// obtains with asynchronous warpgroups, here obtained with the barrier that the K/V pipeline
+// needs anyway.
+//
+// LDS per stage: K (row-major, swizzled) and V (row-major, swizzled), both filled by
+// direct-to-LDS loads, three stages.  While group A runs the MFMA interval of tile t, group B
+// also rewrites V(t) as V^T (two V^T buffers), so that the MFMA intervals fetch every operand
+// with full 16-byte reads: one wave's LDS throughput is bounded by its outstanding requests, and
+// 16-byte requests carry twice the data of the transposing 8-byte reads.
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
+    constexpr int NW = 8, BC = 64, NS = 3;
+    constexpr int BR = NW * 32;          // queries per workgroup
+    constexpr int ROWB = 2 * D;          // bytes per K/V row in LDS
+    constexpr int TILEB = BC * ROWB;     // bytes per K (or V, or V^T) tile
+    constexpr int VTROWB = 2 * BC;       // bytes per V^T row (one dv, BC keys)
+    constexpr int NBLK = TILEB / 1024;   // 1 KiB direct-to-LDS blocks per tile
+    constexpr int BPW = NBLK / NW;       // blocks per wave
+    static_assert(NBLK % NW == 0 && BPW >= 1, "tile shape");
+    static_assert((D / 32) * (BC / 16) % 8 == 0, "V^T chunks split over the eight waves");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS][2][TILEB];   // [stage][K, V]
+    __shared__ __attribute__((aligned(1024))) unsigned char svt[2][TILEB];        // V^T, [tile % 2]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int g = lane >> 5, l32 = lane & 31;
+
+    int L = blockIdx.x;
+    if (p.xcd_remap) L = (blockIdx.x & 7) * (p.num_wg >> 3) + (blockIdx.x >> 3);
+    const int bh = L / p.nqt;
+    int qt = L - bh * p.nqt;
+    if (CAUSAL) qt = p.nqt - 1 - qt;   // heaviest query tiles first
+    const int q0 = qt * BR;
+    const int Sq = p.Sq, Sk = p.Sk;
+    const uint16_t *__restrict__ Qh = p.q + (size_t)bh * Sq * D;
+    const uint16_t *__restrict__ Kh = p.k + (size_t)bh * Sk * D;
+    const uint16_t *__restrict__ Vh = p.v + (size_t)bh * Sk * D;
+    const int qw0 = q0 + wave * 32;   // first query of this wave
+
+    int n_total = (Sk + BC - 1) / BC;
+    int n_full = Sk / BC;
+    if (CAUSAL) {
+        n_total = min(n_total, (min(q0 + BR, Sq) - 1) / BC + 1);
+        n_full = min(n_full, (q0 + 1) / BC);
+    }
+    n_full = min(n_full, n_total);
+
+    // V^T row dv = 32 db + l32 holds chunk kc (8 keys of k-step kc / 2, lane half kc % 2) at chunk
+    // position kc ^ ((dv >> 1) & 7): conflict-free for both the writes and the MFMA reads
+    int grow[BPW], gcol[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int off = (wave * BPW + j) * 1024 + lane * 16;
+        grow[j] = off / ROWB;
+        gcol[j] = ((off % ROWB) >> 4 ^ swz<D>(grow[j])) * 8;
+    }
+    const uint32_t smem0 = lds_addr(&smem[0][0][0]);
+    const uint32_t svt0 = lds_addr(&svt[0][0]);
+
+    auto dma = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * BC;
+        const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            // rows past S_k are clamped onto the last key (masked scores, zero P)
+            const size_t e = (size_t)min(k0 + grow[j], Sk - 1) * D + gcol[j];
+            const uint32_t off = (uint32_t)((wave * BPW + j) * 1024);
+            dma16(Kh + e, st + off);
+            dma16(Vh + e, st + TILEB + off);
+        }
+    };
+
+    // V(t) -> V^T(t): the (dv block, k-step) chunks are split over the 8 waves; each call does
+    // the share of this wave's group (half of the chunks)
+    auto transpose_v = [&](int t) __attribute__((always_inline)) {
+        const uint32_t vr = smem0 + (uint32_t)((t % NS) * 2 * TILEB + TILEB);
+        const uint32_t vt = svt0 + (uint32_t)((t % 2) * TILEB);
+        constexpr int NCH = (D / 32) * (BC / 16);   // (db, ks) pairs
+        const int i = lane & 15, g2 = (lane >> 4) & 1;
+#pragma unroll
+        for (int cc = 0; cc < NCH / 8; ++cc) {
+            const int idx = wave * (NCH / 8) + cc;  // wave-uniform
+            const int db = idx / (BC / 16), ks = idx % (BC / 16);
+            // transposing fetches of two 8-key halves of k-step ks, dv block db (see swz)
+            const int dv = db * 32 + 16 * g2 + 4 * (i & 3);
+            const int r0 = 4 * g + (i >> 2), r1 = r0 + 8;
+            const uint32_t a0 = vr + (ks * 16 + r0) * ROWB + ((((dv >> 3) ^ swz<D>(r0)) << 4) | (((dv >> 2) & 1) << 3));
+            const uint32_t a1 = vr + (ks * 16 + r1) * ROWB + ((((dv >> 3) ^ swz<D>(r1)) << 4) | (((dv >> 2) & 1) << 3));
+            const u32x2 lo = lds_load_tr16<0>(a0);
+            const u32x2 hi = lds_load_tr16<0>(a1);
+            const uint32_t w = vt + (db * 32 + l32) * VTROWB + (((2 * ks + g) ^ ((l32 >> 1) & 7)) << 4);
+            *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)w = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+
+    // prologue: tiles 0 and 1 in flight, then Q^T operands; wait for all; V^T(0)
+    dma(0);
+    if (n_total > 1) dma(1);
+    u32x4 qf[D / 16];
+    {
+        const int row = min(qw0 + l32, Sq - 1);   // rows past S_q: computed, never stored
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qf[ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    wg_barrier();
+    transpose_v(0);
+    // V^T buffer 1 stands for "tile -1" in the first MFMA interval: zeros
+    static_assert(TILEB % (512 * 16) == 0, "V^T zero fill");
+#pragma unroll
+    for (int j = 0; j < TILEB / (512 * 16); ++j)
+        *(__attribute__((address_space(3))) u32x4 *)(uintptr_t)(svt0 + TILEB + (uint32_t)((j * 512 + tid) * 16)) =
+            u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0);
+    wg_barrier();
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float mrow = -INFINITY, lrow = 0.f, lrnd = 0.f;
+    f32x16 s[BC / 32];
+    u32x4 pf[BC / 16];
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) pf[ks] = u32x4{0u, 0u, 0u, 0u};
+    const float c = p.c;
+
+    // a wave whose queries all precede tile t (causal) has nothing to do for it
+    auto active = [&](int t) __attribute__((always_inline)) { return !CAUSAL || t * BC <= qw0 + 31; };
+
+    // The MFMA interval as one operand stream: operations [0, PV_OPS) are O^T += V^T P^T for tile
+    // t-1 (k-step major, 16-byte V^T fetches), operations [PV_OPS, N_OPS) are S^T = K Q^T for tile
+    // t.  READ_AHEAD fetches stay in flight ahead of the MFMA that consumes them (one wave's LDS
+    // throughput is its outstanding fetches over their latency); a scheduling fence after every
+    // operation keeps the compiler to exactly that order and register footprint.
+    constexpr int PV_OPS = (BC / 16) * (D / 32), N_OPS = PV_OPS + (D / 16) * (BC / 32);
+    constexpr int READ_AHEAD = 12;
+    // per-lane parts of the fetch addresses: row base and the swizzled chunk of k-step 0; the
+    // chunk of k-step ks is that chunk XOR 2 ks (k-step ks covers chunks 2 ks and 2 ks + 1)
+    const uint32_t k_row = l32 * ROWB, k_chunk = (uint32_t)((g ^ swz<D>(l32)) << 4);
+    const uint32_t vt_row = l32 * VTROWB, vt_chunk = (uint32_t)((g ^ ((l32 >> 1) & 7)) << 4);
+    auto op_fetch = [&](auto I, uint32_t vt, uint32_t kbase, uint32_t kr, uint32_t kc, uint32_t vr,
+                        uint32_t vc) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < PV_OPS) {
+            constexpr int ks = i / (D / 32), db = i % (D / 32);
+            return lds_load_b128<db * 32 * VTROWB>(vt + vr + (vc ^ (uint32_t)(ks << 5)));
+        } else {
+            constexpr int ks = (i - PV_OPS) / (BC / 32), kb2 = (i - PV_OPS) % (BC / 32);
+            return lds_load_b128<kb2 * 32 * ROWB>(kbase + kr + (kc ^ (uint32_t)(ks << 5)));
+        }
+    };
+    auto op_mfma = [&](auto I, const u32x4 &a) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < PV_OPS) {
+            constexpr int ks = i / (D / 32), db = i % (D / 32);
+            oacc[db] = mfma_32x32x16<T>(a, pf[ks], oacc[db]);
+        } else {
+            constexpr int ks = (i - PV_OPS) / (BC / 32), kb2 = (i - PV_OPS) % (BC / 32);
+            s[kb2] = mfma_32x32x16<T>(a, qf[ks], s[kb2]);
+        }
+    };
+    // Every MFMA interval runs both products, so that the register allocator sees one path: for
+    // t = 0 the V^T buffer of "tile -1" holds zeros and P^T is zero; for t = n_total the scores
+    // are computed from a stale stage and never used; a wave with nothing to add for tile t
+    // (causal) has P^T = 0.
+    auto mfma_phase = [&](int t) __attribute__((always_inline)) {
+        constexpr int R = READ_AHEAD;
+        const uint32_t vt = svt0 + (uint32_t)(((t + 1) % 2) * TILEB);   // V^T of tile t-1
+        const uint32_t kbase = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
+#pragma unroll
+        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
+        // the lane parts pass through an empty asm so that the compiler derives every address
+        // here instead of keeping all of them live across the loop
+        uint32_t kr = k_row, kc = k_chunk, vr = vt_row, vc = vt_chunk;
+        asm volatile("" : "+v"(kr), "+v"(kc), "+v"(vr), "+v"(vc));
+        u32x4 ring[R];
+        static_for<R>([&](auto J) {
+            ring[decltype(J)::value] = op_fetch(J, vt, kbase, kr, kc, vr, vc);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<N_OPS>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const u32x4 a = ring[j % R];
+            if constexpr (j + R < N_OPS)
+                ring[j % R] = op_fetch(std::integral_constant<int, j + R>{}, vt, kbase, kr, kc, vr, vc);
+            op_mfma(J, a);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    auto valu_phase = [&](int t) __attribute__((always_inline)) {
+        if (t >= n_total) return;
+        if (!active(t)) {
+#pragma unroll
+            for (int ks = 0; ks < BC / 16; ++ks) pf[ks] = u32x4{0u, 0u, 0u, 0u};
+            return;
+        }
+        if (t >= n_full) {
+            // element i of block kb2 holds key k0 + 4g + c with c = 32 kb2 + 8 (i / 4) + i % 4 (a
+            // constant); it is visible iff c < lim
+            const int base = t * BC + 4 * g;
+            int lim = Sk - base;
+            if (CAUSAL) lim = min(lim, qw0 + l32 + 1 - base);
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[kb2][i] = -INFINITY;
+        }
+        // row max as a tree of independent v_max3 chains
+        float mq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int kb2 = (k * 8) / 16 % (BC / 32), o = (k * 8) % 16;
+            float m0 = fmaxf(s[kb2][o], s[kb2][o + 1]);
+#pragma unroll
+            for (int i = 2; i < 8; ++i) m0 = fmaxf(m0, s[kb2][o + i]);
+            mq[k] = m0;
+        }
+        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+#pragma unroll
+        for (int kb2 = 2; kb2 < BC / 32; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
+        mx = xhalf_max(mx) * c;
+        if (__builtin_amdgcn_ballot_w64(mx > mrow + RESCALE_LOG2) != 0) {
+            const float mnew = fmaxf(mrow, mx);
+            const float alpha = __builtin_amdgcn_exp2f(mrow - (mnew == -INFINITY ? 0.f : mnew));
+            mrow = mnew;
+            lrow *= alpha;
+            lrnd *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        const float mbase = (mrow == -INFINITY) ? 0.f : mrow;
+        // exponentials, the fp32 row sum as four independent partial sums
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][i], c, -mbase));
+                ls[i & 3] += s[kb2][i];
+            }
+        float lr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int o = h * 8;
+                const u32x4 pk = u32x4{pack2<T>(s[kb2][o + 0], s[kb2][o + 1]), pack2<T>(s[kb2][o + 2], s[kb2][o + 3]),
+                                       pack2<T>(s[kb2][o + 4], s[kb2][o + 5]), pack2<T>(s[kb2][o + 6], s[kb2][o + 7])};
+                pf[kb2 * 2 + h] = pk;
+                if (ATTN_LAZY) lr[h] = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr[h]))));
+            }
+        lrow += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        lrnd += lr[0] + lr[1];
+    };
+
+    // Global interval 2t: A does the MFMA work of tile t, B the softmax of tile t-1 and the V^T of
+    // tile t; interval 2t+1: A the softmax of tile t, B the MFMA work of tile t.  Tile t+1 is
+    // loaded from the start of interval 2t and waited for at the end of interval 2t+1, so it is
+    // in LDS when interval 2t+2 needs its K (QK) and its V (the V^T rewrite).  Both groups pass
+    // the same number of barriers (2 n_total + 3).
+    // (tiles 0 and 1 come from the prologue, so the loads start with tile 2 in interval 2.)
+    if (grp == 0) {
+        for (int t = 0; t <= n_total; ++t) {
+            if (t >= 1 && t + 1 < n_total) dma(t + 1);
+            mfma_phase(t);
+            wg_barrier();
+            if (t >= 1 && t < n_total) transpose_v(t);
+            valu_phase(t);
+            __builtin_amdgcn_s_waitcnt(0);
+            wg_barrier();
+        }
+        wg_barrier();
+    } else {
+        wg_barrier();
+        for (int t = 0; t <= n_total; ++t) {
+            mfma_phase(t);
+            __builtin_amdgcn_s_waitcnt(0);
+            wg_barrier();
+            if (t + 2 < n_total) dma(t + 2);
+            if (t + 1 < n_total) transpose_v(t + 1);
+            valu_phase(t);
+            wg_barrier();
+        }
+    }
+
+    // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
+    const float lt = xhalf_sum(lrow);
+    const float inv = 1.0f / (ATTN_LAZY ? xhalf_sum(lrnd) : lt);
+    const int qrow = qw0 + l32;
+    if (qrow < Sq) {
+        uint16_t *orow = p.o + ((size_t)bh * Sq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int dv = db * 32 + 8 * gi + 4 * g;
+                *reinterpret_cast<u32x2 *>(orow + dv) =
+                    u32x2{pack2<T>(oacc[db][gi * 4 + 0] * inv, oacc[db][gi * 4 + 1] * inv),
+                          pack2<T>(oacc[db][gi * 4 + 2] * inv, oacc[db][gi * 4 + 3] * inv)};
+            }
+        if (p.lse && g == 0) p.lse[(size_t)bh * Sq + qrow] = (mrow + log2f(lt)) * 0.69314718055994530942f;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 
 struct Plan {
-    int block_q, block_k, waves, nqt, num_wg;
+    int qb, nw, ns;              // 32-query blocks per wave (0: ping-pong kernel), waves, LDS stages
+    int block_q, block_k, nqt, num_wg;
 };
 
 int check_common(const void *q, const void *k, const void *v, const void *o, const void *lse, int B, int H, int Sq,
@@ -381,11 +815,42 @@ int check_common(const void *q, const void *k, const void *v, const void *o, con
     return ATTN_OK;
 }
 
-int make_plan(int B, int H, int Sq, int d, Plan *pl) {
-    // first policy: 4 waves x 32 queries; 64 keys per tile at d = 128, 128 at d = 64
-    pl->waves = 4;
-    pl->block_q = 4 * 32;
-    pl->block_k = (d == 128) ? 64 : 128;
+// Tile shapes that are compiled: (query blocks per wave, waves, stages); qb 0 is the ping-pong
+// kernel (8 waves x 32 queries, 3 stages).
+constexpr int kShapes[][3] = {{1, 8, 3}, {1, 8, 4}, {2, 4, 3}, {2, 4, 4}, {1, 4, 2}, {1, 4, 3}, {0, 8, 3}};
+
+// Tile policy per head dimension, measured on MI355X.  ATTN_FWD_POLICY="qb,nw,ns" selects another
+// compiled shape, for tuning.
+void choose_policy(int d, int causal, Plan *pl) {
+    (void)causal;
+    (void)d;
+    pl->qb = 1;
+    pl->nw = 8;
+    pl->ns = 4;
+    static int env[3] = {-1, -1, -1};
+    static std::once_flag once;
+    std::call_once(once, [] {
+        const char *e = std::getenv("ATTN_FWD_POLICY");
+        int a = 0, b = 0, c = 0;
+        if (e && std::sscanf(e, "%d,%d,%d", &a, &b, &c) == 3)
+            for (const auto &sh : kShapes)
+                if (sh[0] == a && sh[1] == b && sh[2] == c) {
+                    env[0] = a;
+                    env[1] = b;
+                    env[2] = c;
+                }
+    });
+    if (env[0] >= 0) {
+        pl->qb = env[0];
+        pl->nw = env[1];
+        pl->ns = env[2];
+    }
+}
+
+int make_plan(int B, int H, int Sq, int d, int causal, Plan *pl) {
+    choose_policy(d, causal, pl);
+    pl->block_q = pl->nw * (pl->qb == 0 ? 1 : pl->qb) * 32;
+    pl->block_k = 64;
     pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
     const long long wg = (long long)pl->nqt * B * H;
     if (wg > INT_MAX) return ATTN_ERR_OVERFLOW;
@@ -393,17 +858,33 @@ int make_plan(int B, int H, int Sq, int d, Plan *pl) {
     return ATTN_OK;
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, int QB, int NW, int NS>
 int launch(const Params &p, const Plan &pl, hipStream_t stream) {
-    constexpr int BC = (D == 128) ? 64 : 128;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, 1, 4, BC, CAUSAL>), dim3(pl.num_wg), dim3(4 * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, NW, 64, NS, CAUSAL>), dim3(pl.num_wg), dim3(NW * 64), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+template <class T, int D, bool CAUSAL>
+int launch_shape(const Params &p, const Plan &pl, hipStream_t s) {
+    const int key = pl.qb * 100 + pl.nw * 10 + pl.ns;
+    switch (key) {
+        case 183: return launch<T, D, CAUSAL, 1, 8, 3>(p, pl, s);
+        case 184: return launch<T, D, CAUSAL, 1, 8, 4>(p, pl, s);
+        case 243: return launch<T, D, CAUSAL, 2, 4, 3>(p, pl, s);
+        case 244: return launch<T, D, CAUSAL, 2, 4, 4>(p, pl, s);
+        case 142: return launch<T, D, CAUSAL, 1, 4, 2>(p, pl, s);
+        case 143: return launch<T, D, CAUSAL, 1, 4, 3>(p, pl, s);
+        case 83:
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<T, D, CAUSAL>), dim3(pl.num_wg), dim3(512), 0, s, p);
+            return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+        default: return ATTN_ERR_UNSUPPORTED;
+    }
 }
 
 template <class T>
 int dispatch(const Params &p, const Plan &pl, int d, int causal, hipStream_t s) {
-    if (d == 128) return causal ? launch<T, 128, true>(p, pl, s) : launch<T, 128, false>(p, pl, s);
-    return causal ? launch<T, 64, true>(p, pl, s) : launch<T, 64, false>(p, pl, s);
+    if (d == 128) return causal ? launch_shape<T, 128, true>(p, pl, s) : launch_shape<T, 128, false>(p, pl, s);
+    return causal ? launch_shape<T, 64, true>(p, pl, s) : launch_shape<T, 64, false>(p, pl, s);
 }
 
 }  // namespace
@@ -414,7 +895,7 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     if (st != ATTN_OK) return st;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     Plan pl;
-    st = make_plan(B, H, S_q, d, &pl);
+    st = make_plan(B, H, S_q, d, causal, &pl);
     if (st != ATTN_OK) return st;
     Params p;
     p.q = static_cast<const uint16_t *>(q);
@@ -449,16 +930,15 @@ extern "C" int attn_fwd_fp8(const void *q, const void *k, const void *v, const f
 
 extern "C" int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, int dtype, int *block_q,
                              int *block_k, int *waves, int *workgroups) {
-    (void)causal;
     if (B < 1 || H < 1 || S_q < 1 || S_k < 1) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
     Plan pl;
-    const int st = make_plan(B, H, S_q, d, &pl);
+    const int st = make_plan(B, H, S_q, d, causal, &pl);
     if (st != ATTN_OK) return st;
     if (block_q) *block_q = pl.block_q;
     if (block_k) *block_k = pl.block_k;
-    if (waves) *waves = pl.waves;
+    if (waves) *waves = pl.nw;
     if (workgroups) *workgroups = pl.num_wg;
     return ATTN_OK;
 }
