@@ -50,6 +50,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // clang vector types (not HIP's u32x4 struct, whose copies go through memory)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 struct BF16 {};
 struct F16 {};
@@ -794,6 +795,300 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Block-scaled fp8 path (the FlashAttention-3 deep dive (techknowgenie), section 4: per-block
+// scale factors, both products in FP8, softmax and accumulation in FP32).
+//
+// Q, K, V hold OCP E4M3 codes; the value of row r of a head is code * descale[r / 128].  One key
+// tile is one descale block (128 keys).  With raw = Q_code . K_code (exact in the fp32 MFMA
+// accumulator), the base-2 score is raw * c_t with c_t = scale * log2(e) * qd * kd_t.  V's
+// descale enters as a per-tile bias of the exponent: the kernel keeps the running max m of
+// raw * c_t + log2(vd_t) and forms p' = exp2(raw * c_t + log2(vd_t) - m) = vd_t * p, so that
+// sum_j p'_j * Vcode_j = sum_j p_j * V_j with no per-tile rescale of O; the row sums take p'
+// times 1 / vd_t.  p' <= 2^RESCALE_LOG2 = 256 fits E4M3 (largest finite 448).
+//
+// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales).  It sums A[i][k] B[k][j] over
+// the pairs (lane half, byte) that A and B share, so any key order that both operands use is
+// valid.  The order used here is the one of the S^T accumulator: byte b of lane half g of
+// k-step kk is key 64 kk + 32 (b / 16) + 8 ((b % 16) / 4) + 4 g + b % 4, so P^T is packed
+// from the accumulator in place, and V^T is fetched with ds_read_b64_tr_b8 (inside each group
+// of 16 lanes, lane j receives byte j % 8 of the 8-byte words addressed by lanes 2 k + j / 8,
+// for k = 0..7).
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+struct ParamsF8 {
+    const uint8_t *q, *k, *v;
+    const float *qd, *kd, *vd;   // descales [b*h][block]; NULL: all ones
+    uint16_t *o;                 // bf16
+    float *lse;
+    int Sq, Sk;
+    int nqb, nkb;                // 128-row blocks of Q and of K/V per head
+    int nqt, num_wg, xcd_remap;
+    float c;                     // scale * log2(e)
+};
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
+    // format 0 (E4M3) for A and B, block scale exponents 127 (2^0)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// four floats -> four E4M3 bytes (round to nearest even), first value in the low byte
+__device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// fp8 tiles sit in LDS row-major (D bytes per key).  The 16-byte chunk c of row r is stored at
+// position c ^ swz8(r).  Every K operand fetch (32 rows x one chunk, two lane halves) and every
+// transposing V fetch (16 rows x 32 bytes) then spreads evenly over the LDS banks.
+template <int D> __device__ __forceinline__ int swz8(int row) {
+    if constexpr (D == 128) return (row >> 1) & 7;
+    else return (row >> 2) & 3;
+}
+
+template <int OFF> __device__ __forceinline__ u32x2 lds_load_tr8(uint32_t addr) {
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(uintptr_t)(addr + OFF));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <int D, int NS, bool CAUSAL>
+__global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
+    constexpr int NW = 8, BC = 128, BR = NW * 32;
+    constexpr int ROWB = D;              // bytes per K/V row
+    constexpr int TILEB = BC * ROWB;     // bytes per K (or V) tile
+    constexpr int NBLK = TILEB / 1024;   // 1 KiB direct-to-LDS blocks per tile
+    constexpr int BPW = NBLK / NW;
+    constexpr int KSTEPS = D / 64;       // k-steps of S^T = K Q^T
+    static_assert(NBLK % NW == 0 && BPW >= 1, "tile shape");
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS][2][TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+
+    int L = blockIdx.x;
+    if (p.xcd_remap) L = (blockIdx.x & 7) * (p.num_wg >> 3) + (blockIdx.x >> 3);
+    const int bh = L / p.nqt;
+    int qt = L - bh * p.nqt;
+    if (CAUSAL) qt = p.nqt - 1 - qt;
+    const int q0 = qt * BR;
+    const int Sq = p.Sq, Sk = p.Sk;
+    const uint8_t *__restrict__ Qh = p.q + (size_t)bh * Sq * D;
+    const uint8_t *__restrict__ Kh = p.k + (size_t)bh * Sk * D;
+    const uint8_t *__restrict__ Vh = p.v + (size_t)bh * Sk * D;
+    const int qw0 = q0 + wave * 32;
+    const float qd = p.qd ? p.qd[(size_t)bh * p.nqb + min(qw0, Sq - 1) / 128] : 1.f;
+    const float cq = p.c * qd;
+
+    // K operand: row l32 of a 32-key block, chunks 4 ks + 2 g and 4 ks + 2 g + 1
+    int koff[2 * KSTEPS];
+#pragma unroll
+    for (int j = 0; j < 2 * KSTEPS; ++j)
+        koff[j] = l32 * ROWB + (((4 * (j >> 1) + 2 * g + (j & 1)) ^ swz8<D>(l32)) << 4);
+    // V^T operand of dv block db: lane m of its 16-lane group fetches 8 bytes of row
+    // 8 (m / 8) + 4 g + (m / 2) % 4 (+ 16 r' per fetch), columns 32 db + 16 ((lane / 16) % 2) + 8 (m % 2)
+    int vlane[D / 32];
+    {
+        const int m = lane & 15, h1 = (lane >> 4) & 1;
+        const int r0 = 8 * (m >> 3) + 4 * g + ((m >> 1) & 3);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            vlane[db] = r0 * ROWB + (((2 * db + h1) ^ swz8<D>(r0)) << 4) + 8 * (m & 1);
+    }
+    int grow[BPW], gcol[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int off = (wave * BPW + j) * 1024 + lane * 16;
+        grow[j] = off / ROWB;
+        gcol[j] = (((off % ROWB) >> 4) ^ swz8<D>(grow[j])) << 4;
+    }
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float mrow = -INFINITY, lrow = 0.f, lrnd = 0.f;
+
+    int n_total = (Sk + BC - 1) / BC;
+    int n_full = Sk / BC;
+    if (CAUSAL) {
+        n_total = min(n_total, (min(q0 + BR, Sq) - 1) / BC + 1);
+        n_full = min(n_full, (q0 + 1) / BC);
+    }
+    n_full = min(n_full, n_total);
+
+    const uint32_t smem0 = lds_addr(&smem[0][0][0]);
+    auto dma = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * BC;
+        const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const size_t e = (size_t)min(k0 + grow[j], Sk - 1) * D + gcol[j];
+            const uint32_t off = (uint32_t)((wave * BPW + j) * 1024);
+            dma16(Kh + e, st + off);
+            dma16(Vh + e, st + TILEB + off);
+        }
+    };
+
+    i32x8 qf[KSTEPS];
+    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+
+    auto compute = [&](int t, uint32_t kt, uint32_t vt, bool masked) __attribute__((always_inline)) {
+        const int k0 = t * BC;
+        const float kdt = p.kd ? p.kd[(size_t)bh * p.nkb + t] : 1.f;
+        const float vdt = p.vd ? p.vd[(size_t)bh * p.nkb + t] : 1.f;
+        // S^T = K Q^T (codes)
+        f32x16 s[BC / 32];
+#pragma unroll
+        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
+        static_for<KSTEPS>([&](auto KS) {
+            constexpr int ks = decltype(KS)::value;
+            static_for<BC / 32>([&](auto KB) {
+                constexpr int kb2 = decltype(KB)::value;
+                const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(kt + koff[2 * ks]);
+                const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(kt + koff[2 * ks + 1]);
+                const i32x8 a = __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                s[kb2] = mfma_f8(a, qf[ks], s[kb2]);
+            });
+        });
+        if (masked) {
+            const int base = k0 + 4 * g;
+            int lim = Sk - base;
+            if (CAUSAL) lim = min(lim, qw0 + l32 + 1 - base);
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[kb2][i] = -INFINITY;
+        }
+        // online softmax of the biased base-2 scores raw * ct + bt
+        const float ct = cq * kdt;
+        const float bt = __builtin_amdgcn_logf(vdt);   // log2
+        const float ivd = __builtin_amdgcn_rcpf(vdt);
+        float mq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float m0 = fmaxf(s[k][0], s[k][1]);
+#pragma unroll
+            for (int i = 2; i < 16; ++i) m0 = fmaxf(m0, s[k][i]);
+            mq[k] = m0;
+        }
+        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+        mx = __builtin_fmaf(xhalf_max(mx), ct, bt);
+        if (__builtin_amdgcn_ballot_w64(mx > mrow + RESCALE_LOG2) != 0) {
+            const float mnew = fmaxf(mrow, mx);
+            const float alpha = __builtin_amdgcn_exp2f(mrow - (mnew == -INFINITY ? 0.f : mnew));
+            mrow = mnew;
+            lrow *= alpha;
+            lrnd *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        const float off = bt - ((mrow == -INFINITY) ? 0.f : mrow);
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][i], ct, off));
+                ls[i & 3] += s[kb2][i];
+            }
+        lrow += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * ivd;
+        // P'^T in E4M3: dword w of k-step kk = keys of s[2 kk + w / 4][4 (w % 4) .. + 3]
+        i32x8 pf[BC / 64];
+#pragma unroll
+        for (int kk = 0; kk < BC / 64; ++kk)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const f32x16 &sv = s[2 * kk + (w >> 2)];
+                const int o = 4 * (w & 3);
+                pf[kk][w] = pack4_e4m3(sv[o], sv[o + 1], sv[o + 2], sv[o + 3]);
+            }
+        // sum of the rounded p' (the weights P.V uses): ones x P'^T on the matrix core
+        f32x16 rs = {};
+#pragma unroll
+        for (int kk = 0; kk < BC / 64; ++kk) rs = mfma_f8(ones, pf[kk], rs);
+        // O^T += V^T P'^T
+        static_for<BC / 64>([&](auto KK) {
+            constexpr int kk = decltype(KK)::value;
+            static_for<D / 32>([&](auto DB) {
+                constexpr int db = decltype(DB)::value;
+                const uint32_t va = vt + vlane[db];
+                const u32x2 r0 = lds_load_tr8<(64 * kk + 0) * ROWB>(va);
+                const u32x2 r1 = lds_load_tr8<(64 * kk + 16) * ROWB>(va);
+                const u32x2 r2 = lds_load_tr8<(64 * kk + 32) * ROWB>(va);
+                const u32x2 r3 = lds_load_tr8<(64 * kk + 48) * ROWB>(va);
+                const i32x8 a = __builtin_bit_cast(i32x8, (u32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]});
+                oacc[db] = mfma_f8(a, pf[kk], oacc[db]);
+            });
+        });
+        lrnd += rs[0] * ivd;
+    };
+
+    constexpr int LPT = 2 * BPW;
+    auto step = [&](int t, bool masked) __attribute__((always_inline)) {
+        const int ahead = min(NS - 2, n_total - 1 - t);
+        if (NS >= 4 && ahead >= 2)
+            wait_vmcnt<2 * LPT>();
+        else if (NS >= 3 && ahead >= 1)
+            wait_vmcnt<LPT>();
+        else
+            wait_vmcnt<0>();
+        wg_barrier();
+        if (t + NS - 1 < n_total) dma(t + NS - 1);
+        if (!masked || !CAUSAL || t * BC <= qw0 + 31) {
+            const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
+            compute(t, st, st + TILEB, masked);
+        }
+    };
+
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+        if (u < n_total) dma(u);
+    {
+        const int row = min(qw0 + l32, Sq - 1);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + 64 * ks + 32 * g);
+            const u32x4 lo = src[0], hi = src[1];
+            qf[ks] = __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    int t = 0;
+    for (; t < n_full; ++t) step(t, false);
+    for (; t < n_total; ++t) step(t, true);
+
+    // lrow holds this lane half's keys; lrnd already sums both halves (the MFMA reduces over k)
+    const float lt = xhalf_sum(lrow);
+    const float inv = 1.0f / lrnd;
+    const int qrow = qw0 + l32;
+    if (qrow < Sq) {
+        uint16_t *orow = p.o + ((size_t)bh * Sq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int dv = db * 32 + 8 * gi + 4 * g;
+                *reinterpret_cast<u32x2 *>(orow + dv) =
+                    u32x2{pack2<BF16>(oacc[db][gi * 4 + 0] * inv, oacc[db][gi * 4 + 1] * inv),
+                          pack2<BF16>(oacc[db][gi * 4 + 2] * inv, oacc[db][gi * 4 + 3] * inv)};
+            }
+        if (p.lse && g == 0) p.lse[(size_t)bh * Sq + qrow] = (mrow + log2f(lt)) * 0.69314718055994530942f;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 
 struct Plan {
@@ -887,12 +1182,63 @@ int dispatch(const Params &p, const Plan &pl, int d, int causal, hipStream_t s) 
     return causal ? launch_shape<T, 64, true>(p, pl, s) : launch_shape<T, 64, false>(p, pl, s);
 }
 
+// fp8: 8 waves x 32 queries, 128-key tiles (one descale block), NS stages
+constexpr int kFp8Stages = 3;
+
+void make_plan_fp8(int B, int H, int Sq, Plan *pl) {
+    pl->qb = 1;
+    pl->nw = 8;
+    pl->ns = kFp8Stages;
+    pl->block_q = 256;
+    pl->block_k = 128;
+    pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
+    pl->num_wg = 0;
+    const long long wg = (long long)pl->nqt * B * H;
+    if (wg <= INT_MAX) pl->num_wg = (int)wg;
+}
+
+template <int D, bool CAUSAL>
+int launch_fp8(const ParamsF8 &p, const Plan &pl, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, kFp8Stages, CAUSAL>), dim3(pl.num_wg), dim3(512), 0, s, p);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int run_fp8(const void *q, const void *k, const void *v, const float *q_descale, const float *k_descale,
+            const float *v_descale, void *o, float *lse, int B, int H, int S_q, int S_k, int d, int causal,
+            float scale, void *stream) {
+    Plan pl;
+    make_plan_fp8(B, H, S_q, &pl);
+    if (pl.num_wg == 0) return ATTN_ERR_OVERFLOW;
+    ParamsF8 p;
+    p.q = static_cast<const uint8_t *>(q);
+    p.k = static_cast<const uint8_t *>(k);
+    p.v = static_cast<const uint8_t *>(v);
+    p.qd = q_descale;
+    p.kd = k_descale;
+    p.vd = v_descale;
+    p.o = static_cast<uint16_t *>(o);
+    p.lse = lse;
+    p.Sq = S_q;
+    p.Sk = S_k;
+    p.nqb = (S_q + 127) / 128;
+    p.nkb = (S_k + 127) / 128;
+    p.nqt = pl.nqt;
+    p.num_wg = pl.num_wg;
+    p.xcd_remap = (pl.num_wg % 8 == 0) ? 1 : 0;
+    p.c = scale * 1.44269504088896340736f;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d == 128) return causal ? launch_fp8<128, true>(p, pl, s) : launch_fp8<128, false>(p, pl, s);
+    return causal ? launch_fp8<64, true>(p, pl, s) : launch_fp8<64, false>(p, pl, s);
+}
+
 }  // namespace
 
 extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S_q,
                         int S_k, int d, int causal, float scale, int dtype, void *stream) {
     int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
     if (st != ATTN_OK) return st;
+    if (dtype == ATTN_FP8_E4M3)
+        return run_fp8(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, S_q, S_k, d, causal, scale, stream);
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     Plan pl;
     st = make_plan(B, H, S_q, d, causal, &pl);
@@ -923,9 +1269,7 @@ extern "C" int attn_fwd_fp8(const void *q, const void *k, const void *v, const f
     if ((reinterpret_cast<uintptr_t>(q_descale) | reinterpret_cast<uintptr_t>(k_descale) |
          reinterpret_cast<uintptr_t>(v_descale)) & 3u)
         return ATTN_ERR_DESCALE;
-    (void)causal;
-    (void)stream;
-    return ATTN_ERR_UNSUPPORTED;
+    return run_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, S_q, S_k, d, causal, scale, stream);
 }
 
 extern "C" int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, int dtype, int *block_q,
@@ -934,8 +1278,13 @@ extern "C" int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, 
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
     Plan pl;
-    const int st = make_plan(B, H, S_q, d, causal, &pl);
-    if (st != ATTN_OK) return st;
+    if (dtype == ATTN_FP8_E4M3) {
+        make_plan_fp8(B, H, S_q, &pl);
+        if (pl.num_wg == 0) return ATTN_ERR_OVERFLOW;
+    } else {
+        const int st = make_plan(B, H, S_q, d, causal, &pl);
+        if (st != ATTN_OK) return st;
+    }
     if (block_q) *block_q = pl.block_q;
     if (block_k) *block_k = pl.block_k;
     if (waves) *waves = pl.nw;

@@ -101,6 +101,9 @@ def test_plan(lib):
     assert n == -(-4096 // bq) * 32
     with pytest.raises(ea.AttnError):
         ea.plan(1, 1, 16, 16, 96)
+    # fp8: one 128-key tile per descale block
+    bq, bk, w, n = ea.plan(2, 16, 4096, 4096, 128, False, dtype=ea.ATTN_FP8_E4M3)
+    assert bk == 128 and bq % 128 == 0 and n == -(-4096 // bq) * 32
 
 
 def test_binding_rejects_host_tensors():

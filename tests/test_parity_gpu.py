@@ -63,6 +63,15 @@ def test_small_full(oracle, shape, dtype, causal):
     assert st["pass"], st
 
 
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_full_fp8(oracle, shape, causal):
+    B, H, Sq, Sk, d = shape
+    w = I.random_workload(B, H, Sq, Sk, d, "fp8", causal, seed=2000 + Sq + 7 * Sk + d)
+    st = _run_full(oracle, w)
+    assert st["pass"], st
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_outliers_small(oracle, causal):
     w = I.random_workload(1, 2, 700, 700, 64, "bf16", causal, seed=55, outliers=True)
@@ -114,9 +123,7 @@ def test_deterministic(oracle):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("name", [
-    pytest.param(n, marks=pytest.mark.skip(reason="attn_fwd_fp8 kernel not built yet (returns ATTN_ERR_UNSUPPORTED)"))
-    if I.WORKLOADS[n].dtype == "fp8" else n for n in sorted(I.WORKLOADS)])
+@pytest.mark.parametrize("name", sorted(I.WORKLOADS))
 def test_workload_sampled_rows(oracle, name):
     """Full-size workloads in the benchmark's launch configuration, checked on sampled rows."""
     w = I.WORKLOADS[name]
