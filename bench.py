@@ -158,7 +158,7 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": counter_traffic(work.name),
-            "kernel": "attn_fwd_kernel",
+            "kernel": "attn_fwd_fp8_kernel" if work.dtype == "fp8" else "attn_fwd_kernel",
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
             "min_launch_us": round(float(np.min(per_launch)) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,
