@@ -43,8 +43,10 @@
  *                            and the online forms agree.
  * plus oracle_decode_e4m3_blocks (fp8 input decoding, OCP E4M3 "fn" format
  * with per-(b, h, 128-row block) fp32 descale; the deep dive's section 4
- * block quantisation) and oracle_softmax_block (exposes one explicit P block
- * so tests can check that softmax rows sum to one).
+ * block quantisation), oracle_quantize_e4m3_blocks (the block quantisation
+ * itself: per-block |max|, descale, nearest code) and oracle_softmax_block
+ * (exposes one explicit P block so tests can check that softmax rows sum to
+ * one).
  */
 #include <math.h>
 #include <pthread.h>
@@ -302,6 +304,60 @@ int oracle_decode_e4m3_blocks(const uint8_t *codes, const float *descale, int B,
                 const int64_t idx = (bh * S + r) * (int64_t)d + t;
                 out[idx] = oracle_e4m3_value(codes[idx]) * ds;
             }
+        }
+    return 0;
+}
+
+/*
+ * The finite E4M3 code nearest to the real value x, ties to the even code
+ * (round to nearest even), found by scanning every finite non-negative code
+ * (0x00 .. 0x7e).  Magnitudes above 448 get 448 (the nearest finite value),
+ * i.e. the encoding saturates.  The sign bit is x's sign bit (-0 -> 0x80).
+ */
+uint8_t oracle_e4m3_encode(double x) {
+    const double a = fabs(x);
+    int best = 0;
+    double best_err = a;   /* code 0 has value 0 */
+    for (int c = 1; c <= 0x7e; ++c) {
+        const double err = fabs(oracle_e4m3_value((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+}
+
+/*
+ * Block quantisation of a [B][H][S][d] fp32 tensor (the deep dive's section 4:
+ * one scale per block from the block's local maximum): for each (b, h, block
+ * of blk rows), amax = max |x| over the block (rows past S do not exist),
+ * descale = amax / 448 as a float (448 = largest finite E4M3), or 1 when
+ * amax = 0; code = oracle_e4m3_encode(x / descale).  The quotient is taken in
+ * double: the exact quotient of two floats that is not exactly an E4M3
+ * midpoint lies at least 2^-29 (relative) away from every midpoint, far
+ * beyond the 2^-53 of the double rounding, so the code is that of the exact
+ * quotient.
+ */
+int oracle_quantize_e4m3_blocks(const float *x, int B, int H, int S, int d, int blk, uint8_t *codes, float *descale) {
+    if (!x || !codes || !descale || B < 1 || H < 1 || S < 1 || d < 1 || blk < 1) return -1;
+    const int nblk = (S + blk - 1) / blk;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
+        for (int j = 0; j < nblk; ++j) {
+            const int r0 = j * blk, r1 = (r0 + blk < S) ? r0 + blk : S;
+            float amax = 0.0f;
+            for (int r = r0; r < r1; ++r)
+                for (int t = 0; t < d; ++t) {
+                    const float v = fabsf(x[(bh * S + r) * (int64_t)d + t]);
+                    if (v > amax) amax = v;
+                }
+            const float ds = amax > 0.0f ? amax / 448.0f : 1.0f;
+            descale[bh * nblk + j] = ds;
+            for (int r = r0; r < r1; ++r)
+                for (int t = 0; t < d; ++t) {
+                    const int64_t idx = (bh * S + r) * (int64_t)d + t;
+                    codes[idx] = oracle_e4m3_encode((double)x[idx] / (double)ds);
+                }
         }
     return 0;
 }

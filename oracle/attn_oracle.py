@@ -73,6 +73,10 @@ class Oracle:
         L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         L.oracle_decode_e4m3_blocks.restype = ci
         L.oracle_decode_e4m3_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ci] * 5 + [_dptr]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_quantize_e4m3_blocks.restype = ci
+        L.oracle_quantize_e4m3_blocks.argtypes = [ctypes.c_void_p] + [ci] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
         self.L = L
         self.last_threads = 0
 
@@ -154,6 +158,23 @@ class Oracle:
         if r < 0:
             raise ValueError("oracle rejected arguments")
         return out
+
+
+    def e4m3_encode(self, x) -> np.ndarray:
+        """Nearest finite E4M3 code (ties to even, saturating) of each value of x (any shape)."""
+        x = np.asarray(x, dtype=np.float64)
+        return np.array([self.L.oracle_e4m3_encode(float(v)) for v in x.reshape(-1)], dtype=np.uint8).reshape(x.shape)
+
+    def quantize_e4m3_blocks(self, x, blk: int = 128):
+        """Block quantisation of fp32 x [B,H,S,d] -> (codes uint8 [B,H,S,d], descale fp32 [B,H,ceil(S/blk)])."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+        B, H, S, d = x.shape
+        codes = np.empty(x.shape, np.uint8)
+        descale = np.empty((B, H, (S + blk - 1) // blk), np.float32)
+        r = self.L.oracle_quantize_e4m3_blocks(x.ctypes.data, B, H, S, d, blk, codes.ctypes.data, descale.ctypes.data)
+        if r < 0:
+            raise ValueError("oracle rejected arguments")
+        return codes, descale
 
 
 _default: Oracle | None = None

@@ -286,6 +286,63 @@ def check_large_scores(oracle):
         assert np.all(np.isfinite(o)) and np.abs(o - ref).max() <= 1e-12
 
 
+def check_e4m3_encode(oracle):
+    """Nearest-even E4M3 encoding against torch's float8_e4m3fn cast (round to nearest even from
+    fp32): every finite value, every midpoint between neighbours (exact ties), the floats next to
+    each midpoint, random floats in range, both signs; saturation above 448; code round trip."""
+    tab = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    vals = tab[[c for c in range(127)]]                      # 0 .. 448, code order
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)   # exact in fp32
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    rng = np.random.Generator(np.random.PCG64(1300))
+    rnd = np.concatenate([rng.uniform(0, 448, 4000), np.exp2(rng.uniform(-12, 8.8, 4000))]).astype(np.float32)
+    pos = np.concatenate([vals.astype(np.float32), mids, up, dn, rnd])
+    pos = pos[pos <= 448]
+    x = np.concatenate([pos, -pos]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(x.astype(np.float64))
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:5]]
+    big = np.array([448.001, 449.0, 463.99, 464.0, 500.0, 1e4, 3e38])
+    assert np.all(oracle.e4m3_encode(big) == 0x7E) and np.all(oracle.e4m3_encode(-big) == 0xFE)
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    assert np.array_equal(oracle.e4m3_encode(tab[finite]), np.array(finite, dtype=np.uint8))
+
+
+def check_quantize_blocks(oracle):
+    """Block quantisation against the input generator's independent quantiser, and its defining
+    relations: descale = fp32(amax) / fp32(448) (1 for an all-zero block), the element of largest
+    |x| gets the largest code (448), the ragged last block has its own scale, and every decoded
+    value is within half a code step of x."""
+    from exact_attention_32_amd import inputs as I
+
+    rng = np.random.Generator(np.random.PCG64(1400))
+    B, H, S, d = 2, 3, 300, 16
+    x = rng.standard_normal((B, H, S, d), dtype=np.float32)
+    x[:, :, 128:256] *= np.float32(37.5)          # blocks of different scales
+    x[1, 2, 0:128] = 0.0                          # an all-zero block
+    x[0, 1, 130, 3] = -1000.0                     # a block whose |max| is negative
+    codes, ds = oracle.quantize_e4m3_blocks(x)
+    rc, rd = I.quantize_e4m3_blocks(x)
+    assert np.array_equal(codes, rc) and np.array_equal(ds, rd)
+    tab = oracle.e4m3_table()
+    for b in range(B):
+        for h in range(H):
+            for j in range(3):
+                xb = x[b, h, j * 128:(j + 1) * 128]
+                amax = np.float32(np.abs(xb).max())
+                want = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+                assert ds[b, h, j] == want
+                cb = codes[b, h, j * 128:(j + 1) * 128]
+                if amax > 0:
+                    assert (cb.reshape(-1)[np.argmax(np.abs(xb))] & 0x7F) == 0x7E
+                dec = tab[cb] * np.float64(ds[b, h, j])
+                step = np.maximum(np.abs(xb.astype(np.float64)) * 2.0 ** -3, 2.0 ** -9 * np.float64(ds[b, h, j]))
+                assert np.all(np.abs(dec - xb) <= step / 2 * (1 + 1e-12))
+    assert np.all(codes[1, 2, 0:128] == 0) and ds[1, 2, 0] == 1.0
+
+
 ALL_CHECKS = [
     check_sdpa_fp64,
     check_lse_logsumexp,
@@ -298,6 +355,8 @@ ALL_CHECKS = [
     check_online_equals_two_pass,
     check_rows_mode,
     check_e4m3_decode,
+    check_e4m3_encode,
+    check_quantize_blocks,
     check_decode_blocks,
     check_large_scores,
 ]

@@ -34,6 +34,15 @@ MUTANTS = {
     "e4m3_subnormal": ("if (e == 0) mag = ldexp((double)m / 8.0, -6);", "if (e == 0) mag = ldexp((double)m / 8.0, -7);"),
     "e4m3_sign": ("return s ? -mag : mag;", "return mag;"),
     "descale_block_index": ("descale[bh * nblk + r / blk]", "descale[bh * nblk + (r + 1) / blk]"),
+    "e4m3_ties_to_odd": ("(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    "e4m3_scan_short": ("for (int c = 1; c <= 0x7e; ++c) {", "for (int c = 1; c <= 0x77; ++c) {"),
+    "e4m3_sign_dropped": ("return (uint8_t)(best | (signbit(x) ? 0x80 : 0));", "return (uint8_t)best;"),
+    "quant_descale_240": ("const float ds = amax > 0.0f ? amax / 448.0f : 1.0f;",
+                          "const float ds = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    "quant_block_short": ("const int r0 = j * blk, r1 = (r0 + blk < S) ? r0 + blk : S;",
+                          "const int r0 = j * blk, r1 = (r0 + blk < S) ? r0 + blk - 1 : S;"),
+    "quant_amax_signed": ("const float v = fabsf(x[(bh * S + r) * (int64_t)d + t]);",
+                          "const float v = x[(bh * S + r) * (int64_t)d + t];"),
 }
 
 
