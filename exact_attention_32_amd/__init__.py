@@ -15,7 +15,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 
-ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3, ATTN_F32 = 0, 1, 2, 3
 
 _lib = None
 
@@ -42,6 +42,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.attn_status_string.argtypes = [ci]
     L.attn_fwd_plan.restype = ci
     L.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci] + [ctypes.POINTER(ci)] * 4
+    L.attn_quantize_e4m3.restype = ci
+    L.attn_quantize_e4m3.argtypes = [vp, ci, vp, vp, ci, ci, ci, ci, vp]
     if path == LIB_PATH:
         _lib = L
     return L
@@ -131,3 +133,28 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scal
                                      int(bool(causal)), float(scale), _stream(q.device))
     _check(rc)
     return out, lse
+
+
+def quantize_e4m3(x: torch.Tensor, codes: torch.Tensor | None = None, descale: torch.Tensor | None = None):
+    """Per-(b, h, 128-row block) E4M3 quantisation of x [B, H, S, d] (fp32, bf16 or fp16) on the GPU.
+
+    Returns (codes uint8 [B, H, S, d], descale fp32 [B, H, ceil(S/128)]), the inputs of fwd_fp8.
+    """
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, S, d] device tensor")
+    dt = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    B, H, S, d = x.shape
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty((B, H, (S + 127) // 128), dtype=torch.float32, device=x.device)
+    if codes.shape != x.shape or codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous uint8 tensor of x's shape")
+    if tuple(descale.shape) != (B, H, (S + 127) // 128) or descale.dtype != torch.float32 or not descale.is_contiguous():
+        raise ValueError("descale must be a contiguous fp32 tensor [B, H, ceil(S/128)]")
+    rc = load_library().attn_quantize_e4m3(x.data_ptr(), dt, codes.data_ptr(), descale.data_ptr(), B, H, S, d,
+                                           _stream(x.device))
+    _check(rc)
+    return codes, descale

@@ -7,6 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SOURCES = [SRC, os.path.join(PKG, "csrc", "quantize.hip")]
 LIB = os.path.join(PKG, "libattn_fwd.so")
 
 HIPCC_FLAGS = [
@@ -24,7 +25,7 @@ HIPCC_FLAGS = [
 
 def build(out: str = LIB, extra: list[str] | None = None) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *(extra or []), SRC, "-o", out + ".tmp"]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *(extra or []), *SOURCES, "-o", out + ".tmp"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out

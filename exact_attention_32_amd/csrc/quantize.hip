@@ -1,0 +1,164 @@
+// quantize.hip -- per-block E4M3 quantisation on MI355X (gfx950).
+//
+// The step before the block-scaled fp8 attention: one fp32 scale per
+// (batch, head, 128-row block) taken from the block's largest |x|
+// (FlashAttention-3 deep dive (techknowgenie), section 4, block quantisation),
+// descale = amax / 448 (448 = largest finite E4M3; 1 for an all-zero block),
+// code = the E4M3 value nearest to x / descale, ties to even, saturating.
+//
+// The path is HBM-bound (4, 2 or 2 bytes in and 1 byte out per element), so the
+// kernel is one read of the block into registers, one reduction, one write:
+// a workgroup of 256 threads owns one 128-row block (128 x d elements), each
+// thread holds d/8 groups of 4 consecutive elements (coalesced 16- or 8-byte
+// loads, 4-byte code stores).
+//
+// Exact rounding: the fp32 quotient q = RN(x / descale) and the exact quotient
+// lie on the same side of every E4M3 midpoint unless q is itself a midpoint
+// (a midpoint between them would be a closer float), so only then is the exact
+// residual x - q * descale (one FMA, exact for a correctly rounded quotient)
+// consulted, and q is moved one float towards the exact quotient before the
+// hardware's round-to-nearest-even conversion.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "attn.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int QBLK = 128;    // rows per scale block
+constexpr int QTHREADS = 256;
+
+template <class In> __device__ __forceinline__ f32x4 load4(const In *p);
+template <> __device__ __forceinline__ f32x4 load4<float>(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+// 16-bit storage types (2 bytes, so that pointer arithmetic counts elements); a bfloat16 value
+// is the upper half of a float
+struct bf16_t {
+    uint16_t bits;
+};
+struct f16_t {
+    uint16_t bits;
+};
+static_assert(sizeof(bf16_t) == 2 && sizeof(f16_t) == 2, "16-bit element types");
+template <> __device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t *p) {
+    const u16x4 v = *reinterpret_cast<const u16x4 *>(p);
+    return f32x4{__uint_as_float((uint32_t)v[0] << 16), __uint_as_float((uint32_t)v[1] << 16),
+                 __uint_as_float((uint32_t)v[2] << 16), __uint_as_float((uint32_t)v[3] << 16)};
+}
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <> __device__ __forceinline__ f32x4 load4<f16_t>(const f16_t *p) {
+    const f16x4 v = *reinterpret_cast<const f16x4 *>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// x / ds as the float that the hardware's nearest-even conversion maps to the code of the exact
+// quotient (see the file comment); |result| <= 448
+__device__ __forceinline__ float quotient(float x, float ds) {
+    float q = x / ds;   // correctly rounded division
+    const float a = fabsf(q);
+    if (a >= 448.0f) return copysignf(448.0f, q);
+    bool mid;
+    if (a >= 0x1p-6f) {
+        // normal E4M3 range: 3 mantissa bits kept, the next one set, the rest zero
+        mid = (__float_as_uint(a) & 0xFFFFFu) == 0x80000u;
+    } else {
+        // subnormal E4M3 range: midpoints are the odd multiples of 2^-10
+        const float t = a * 1024.0f;
+        mid = (t == truncf(t)) && (((int)t & 1) != 0);
+    }
+    if (mid) {
+        const float r = fmaf(-q, ds, x);   // exact residual
+        if (r != 0.0f)
+            q = __uint_as_float(__float_as_uint(q) + (((r > 0.0f) == (q > 0.0f)) ? 1u : 0xFFFFFFFFu));
+    }
+    return q;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+template <int D, class In>
+__global__ __launch_bounds__(QTHREADS) void quantize_e4m3_kernel(const In *__restrict__ x, uint32_t *__restrict__ codes,
+                                                                 float *__restrict__ descale, int S, int nblk) {
+    constexpr int PER = QBLK * D / 4 / QTHREADS;   // groups of 4 elements per thread
+    static_assert(PER * 4 * QTHREADS == QBLK * D, "block shape");
+    const int tid = threadIdx.x;
+    const int blk = blockIdx.x;
+    const int bh = blk / nblk, j = blk - bh * nblk;
+    const int r0 = j * QBLK;
+    const int rows = min(QBLK, S - r0);
+    const size_t base = ((size_t)bh * S + r0) * D;   // first element of the block
+
+    f32x4 v[PER];
+    float amax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int g = tid + p * QTHREADS;   // group index inside the block
+        if ((4 * g) / D < rows) {
+            v[p] = load4<In>(x + base + 4 * g);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[p][0]), fabsf(v[p][1])), fmaxf(fabsf(v[p][2]), fabsf(v[p][3]))));
+        } else {
+            v[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __shared__ float red[QTHREADS / 64];
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float ds = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (tid == 0) descale[blk] = ds;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int g = tid + p * QTHREADS;
+        if ((4 * g) / D < rows) {
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(v[p][0], ds), quotient(v[p][1], ds), 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(v[p][2], ds), quotient(v[p][3], ds), w, true);
+            codes[(base + 4 * g) / 4] = (uint32_t)w;
+        }
+    }
+}
+
+template <int D>
+int launch_quant(const void *x, int dtype, void *codes, float *descale, int nwg, int S, int nblk, hipStream_t s) {
+    uint32_t *c = static_cast<uint32_t *>(codes);
+    if (dtype == ATTN_F32)
+        hipLaunchKernelGGL((quantize_e4m3_kernel<D, float>), dim3(nwg), dim3(QTHREADS), 0, s,
+                           static_cast<const float *>(x), c, descale, S, nblk);
+    else if (dtype == ATTN_BF16)
+        hipLaunchKernelGGL((quantize_e4m3_kernel<D, bf16_t>), dim3(nwg), dim3(QTHREADS), 0, s,
+                           static_cast<const bf16_t *>(x), c, descale, S, nblk);
+    else
+        hipLaunchKernelGGL((quantize_e4m3_kernel<D, f16_t>), dim3(nwg), dim3(QTHREADS), 0, s,
+                           static_cast<const f16_t *>(x), c, descale, S, nblk);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
+                                  void *stream) {
+    if (!x || !codes) return ATTN_ERR_NULL;
+    if (!descale) return ATTN_ERR_DESCALE;
+    if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15u) return ATTN_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(descale) & 3u) return ATTN_ERR_DESCALE;
+    const long long nblk = (S + QBLK - 1) / QBLK;
+    const long long nwg = (long long)B * H * nblk;
+    if (nwg > INT_MAX || (long long)B * H > INT_MAX / S) return ATTN_ERR_OVERFLOW;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d == 128) return launch_quant<128>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
+    return launch_quant<64>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
+}

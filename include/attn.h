@@ -37,7 +37,8 @@ extern "C" {
 typedef enum {
     ATTN_F16 = 0,       /* q, k, v, o are IEEE binary16 */
     ATTN_BF16 = 1,      /* q, k, v, o are bfloat16 */
-    ATTN_FP8_E4M3 = 2   /* q, k, v are OCP E4M3 codes (unit descales), o is bfloat16 */
+    ATTN_FP8_E4M3 = 2,  /* q, k, v are OCP E4M3 codes (unit descales), o is bfloat16 */
+    ATTN_F32 = 3        /* IEEE binary32: an input type of attn_quantize_e4m3 only */
 } attn_dtype;
 
 typedef enum {
@@ -80,6 +81,25 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
 int attn_fwd_fp8(const void *q, const void *k, const void *v, const float *q_descale, const float *k_descale,
                  const float *v_descale, void *o, float *lse, int B, int H, int S_q, int S_k, int d, int causal,
                  float scale, void *stream);
+
+/*
+ * Block quantisation to OCP E4M3, the input preparation of attn_fwd_fp8 (the
+ * FlashAttention-3 deep dive, section 4: one scale per block, from the block's
+ * largest magnitude).  For every (b, h) and block of 128 rows of
+ * x[B][H][S][d] (the last block may be shorter):
+ *   amax       = max |x| over the block
+ *   descale    = amax / 448 in fp32 (448 = largest finite E4M3), 1 if amax == 0
+ *   codes[...] = the E4M3 code nearest to x / descale (exact quotient), ties
+ *                to even, saturating at +-448; the sign of x is kept (-0 -> 0x80)
+ *   x       : device pointer, dtype ATTN_F32, ATTN_BF16 or ATTN_F16, 16-byte aligned
+ *   codes   : device pointer, uint8 [B][H][S][d], 16-byte aligned
+ *   descale : device pointer, fp32 [B][H][ceil(S/128)], 4-byte aligned
+ *   d       : 64 or 128; stream: hipStream_t or NULL
+ * The outputs are exactly what attn_fwd_fp8 takes.  x must be finite.
+ * Returns an attn_status (ATTN_ERR_DESCALE for a NULL or misaligned descale).
+ */
+int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
+                       void *stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char *attn_status_string(int status);

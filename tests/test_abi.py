@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_fwd_plan"}
+    assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_fwd_plan", "attn_quantize_e4m3"}
     for n in names:
         assert hasattr(lib, n), f"library does not export {n}"
 
@@ -112,3 +112,17 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.fwd(q, q, q)
+
+
+def callq(lib, x=P, dtype=3, codes=P, ds=P, B=1, H=1, S=16, d=128):
+    return lib.attn_quantize_e4m3(x, dtype, codes, ds, B, H, S, d, None)
+
+
+def test_quantize_validation(lib):
+    assert callq(lib, x=None) == NULL and callq(lib, codes=None) == NULL
+    assert callq(lib, ds=None) == DESCALE and callq(lib, ds=P + 2) == DESCALE
+    for kw in ("B", "H", "S"):
+        assert callq(lib, **{kw: 0}) == SHAPE
+    assert callq(lib, d=96) == UNSUP and callq(lib, dtype=2) == UNSUP and callq(lib, dtype=7) == UNSUP
+    assert callq(lib, x=P + 4) == ALIGN and callq(lib, codes=P + 8) == ALIGN
+    assert callq(lib, B=2 ** 16, H=2 ** 16, S=2 ** 10) == OVERFLOW

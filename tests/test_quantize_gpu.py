@@ -1,0 +1,95 @@
+"""GPU parity of the per-block E4M3 quantiser: bit-exact against the oracle's quantiser.
+
+Codes and descales are integer / exactly specified outputs, so the bar is
+equality: fp32 inputs are compared with the oracle run on the same fp32
+values; bf16 and fp16 inputs with the oracle run on their exact fp32 values.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn_oracle
+from tests import parity_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_32_amd as ea
+
+    ea.load_library()
+    return attn_oracle.get()
+
+
+def _draw(shape, seed, spread=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if spread:
+        # blocks of very different magnitude, a few large and tiny entries, exact ties
+        B, H, S, d = shape
+        for j in range(0, S, 128):
+            x[:, :, j:j + 128] *= np.float32(2.0 ** rng.integers(-20, 20))
+        x.reshape(-1)[rng.choice(x.size, size=min(64, x.size), replace=False)] *= np.float32(1e3)
+    return x
+
+
+def _check(oracle, x32: np.ndarray, dtype: torch.dtype):
+    import exact_attention_32_amd as ea
+
+    xt = torch.from_numpy(x32).to(dtype)
+    exact32 = xt.float().numpy()          # the exact values the kernel sees
+    codes, ds = ea.quantize_e4m3(xt.to("cuda:0"))
+    torch.cuda.synchronize()
+    rc, rd = oracle.quantize_e4m3_blocks(exact32)
+    gc, gd = codes.cpu().numpy(), ds.cpu().numpy()
+    assert np.array_equal(gd, rd), np.argwhere(gd != rd)[:5]
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, [(tuple(i), float(exact32[tuple(i)]), int(gc[tuple(i)]), int(rc[tuple(i)])) for i in bad[:5]]
+
+
+SHAPES = [(1, 1, 1, 64), (1, 2, 127, 128), (2, 3, 300, 64), (1, 2, 513, 128), (2, 2, 1024, 128)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16], ids=["f32", "bf16", "f16"])
+def test_quantize_matches_oracle(oracle, shape, dtype):
+    x = _draw(shape, 3000 + sum(shape))
+    if dtype == torch.float16:
+        x = np.clip(x, -6e4, 6e4)
+    U.say(f"[gpu] quantize {shape} {dtype}")
+    _check(oracle, x, dtype)
+
+
+def test_quantize_special_blocks(oracle):
+    """All-zero block (descale 1), negative zero, exact E4M3 midpoints after scaling, saturation edge."""
+    x = np.zeros((1, 1, 384, 64), np.float32)
+    # block 1: values that are exact midpoints of the scaled grid (amax = 448 -> descale 1)
+    tab = torch.arange(128, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()[:127]
+    mids = ((tab[:-1] + tab[1:]) / 2).astype(np.float32)
+    blk = x[0, 0, 128:256].reshape(-1)
+    blk[:mids.size] = mids
+    blk[mids.size:2 * mids.size] = -mids
+    blk[-1] = 448.0
+    # block 2: -0.0 entries and values around the largest code
+    b2 = x[0, 0, 256:384].reshape(-1)
+    b2[:] = np.float32(-0.0)
+    b2[0:4] = [1.0, -1.0, 0.999, 1.0001]
+    U.say("[gpu] quantize special blocks")
+    _check(oracle, x, torch.float32)
+
+
+def test_quantized_inputs_drive_fp8_attention(oracle):
+    """quantize_e4m3 -> fwd_fp8 reproduces the fp8 path of the input generator (same codes)."""
+    import exact_attention_32_amd as ea
+    from exact_attention_32_amd import inputs as I
+
+    w = I.random_workload(1, 2, 200, 200, 128, "fp8", False, seed=77)
+    x = I.make_inputs(w)
+    dev = "cuda:0"
+    qc, qd = ea.quantize_e4m3(torch.from_numpy(x.q32).to(dev))
+    assert torch.equal(qc.cpu(), x.q) and torch.equal(qd.cpu(), x.q_descale)
+    o1, l1 = ea.fwd_fp8(qc, x.k.to(dev), x.v.to(dev), qd, x.k_descale.to(dev), x.v_descale.to(dev), scale=w.scale)
+    o2, l2 = U.run_gpu(x)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
