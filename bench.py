@@ -104,6 +104,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--quantize", action="store_true",
+                    help="instead of the attention benchmark, time the per-block E4M3 quantiser on the fp32 Q, K, V "
+                         "of the fp8 workload (HBM-bound; reports GB/s)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -117,6 +120,8 @@ def main(argv=None):
 
     if args.copy_calibration > 0:
         return copy_calibration(args.copy_calibration, max(1, args.steps))
+    if args.quantize:
+        return bench_quantize(args.steps, args.warmup, not args.no_cpu_baseline)
 
     import numpy as np
 
@@ -183,6 +188,71 @@ def copy_calibration(mib: int, reps: int) -> int:
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
                       "launches": reps}), flush=True)
+    return 0
+
+
+def bench_quantize(steps: int, warmup: int, cpu: bool) -> int:
+    """One step = E4M3 block quantisation of the fp32 Q, K and V of the fp8 workload (three launches)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_32_amd as ea
+    from exact_attention_32_amd import inputs as I
+
+    work = I.WORKLOADS["fp8_b2_h16_s4096_d128"]
+    x = I.make_inputs(work)
+    dev = torch.device("cuda:0")
+    srcs = [torch.from_numpy(a).to(dev) for a in (x.q32, x.k32, x.v32)]
+    outs = [(torch.empty(t.shape, dtype=torch.uint8, device=dev),
+             torch.empty((work.B, work.H, (t.shape[2] + 127) // 128), dtype=torch.float32, device=dev)) for t in srcs]
+
+    def step():
+        for t, (c, d) in zip(srcs, outs):
+            ea.quantize_e4m3(t, c, d)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    elems = sum(t.numel() for t in srcs)
+    nblk = sum(d.numel() for _, d in outs)
+    alg_bytes = elems * (4 + 1) + nblk * 4      # fp32 in, code out, descale out, each once
+    ms_step = wall * 1e3 / steps
+    avg = float(np.mean(per))
+    result = {
+        "metric": "fp8 block quantisation of Q, K, V (HBM GB/s)",
+        "value": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32->e4m3",
+        "data": "synthetic (the fp32 N(0,1) draws of the fp8 workload)",
+        "config": {"workload": "quantize_" + work.name, "tensors": 3, "shape": list(srcs[0].shape)},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (avg * 1e-3) / 1e9, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(alg_bytes / (avg * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "kernel": "quantize_e4m3_kernel (3 launches per step)", "avg_step_us": round(avg * 1e3, 2),
+                     "algorithmic_bytes_per_step": alg_bytes},
+    }
+    if cpu:
+        from oracle import attn_oracle
+
+        orc = attn_oracle.get()
+        a = np.ascontiguousarray(x.q32[:1, :2])   # 2 heads of Q
+        t1 = time.perf_counter()
+        orc.quantize_e4m3_blocks(a)
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(a.size * 5 / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"2 of 32 (b,h) heads of Q ({a.size} elements), single-threaded; {dt:.2f} s"}
+    print(json.dumps(result), flush=True)
     return 0
 
 

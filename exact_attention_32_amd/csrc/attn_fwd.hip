@@ -940,8 +940,25 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
 
     auto compute = [&](int t, uint32_t kt, uint32_t vt, bool masked) __attribute__((always_inline)) {
         const int k0 = t * BC;
-        const float kdt = p.kd ? p.kd[(size_t)bh * p.nkb + t] : 1.f;
-        const float vdt = p.vd ? p.vd[(size_t)bh * p.nkb + t] : 1.f;
+        // the per-lane offsets pass through an empty asm here, so that the compiler forms each
+        // fetch address as lane offset + stage base + immediate inside the tile instead of keeping
+        // every (offset + immediate) sum live in its own register across the loop
+        int ko[2 * KSTEPS], vo[D / 32];
+#pragma unroll
+        for (int j = 0; j < 2 * KSTEPS; ++j) {
+            ko[j] = koff[j];
+            asm volatile("" : "+v"(ko[j]));
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            vo[db] = vlane[db];
+            asm volatile("" : "+v"(vo[db]));
+        }
+        // descales through the constant address space: wave-uniform scalar loads, which the
+        // vector-memory counter that paces the K/V pipeline does not see
+        typedef const __attribute__((address_space(4))) float cfloat;
+        const float kdt = p.kd ? ((cfloat *)p.kd)[(size_t)bh * p.nkb + t] : 1.f;
+        const float vdt = p.vd ? ((cfloat *)p.vd)[(size_t)bh * p.nkb + t] : 1.f;
         // S^T = K Q^T (codes)
         f32x16 s[BC / 32];
 #pragma unroll
@@ -952,8 +969,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             constexpr int ks = decltype(KS)::value;
             static_for<BC / 32>([&](auto KB) {
                 constexpr int kb2 = decltype(KB)::value;
-                const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(kt + koff[2 * ks]);
-                const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(kt + koff[2 * ks + 1]);
+                const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(kt + ko[2 * ks]);
+                const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(kt + ko[2 * ks + 1]);
                 const i32x8 a = __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
                 s[kb2] = mfma_f8(a, qf[ks], s[kb2]);
             });
@@ -1017,19 +1034,27 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
         f32x16 rs = {};
 #pragma unroll
         for (int kk = 0; kk < BC / 64; ++kk) rs = mfma_f8(ones, pf[kk], rs);
-        // O^T += V^T P'^T
-        static_for<BC / 64>([&](auto KK) {
-            constexpr int kk = decltype(KK)::value;
-            static_for<D / 32>([&](auto DB) {
-                constexpr int db = decltype(DB)::value;
-                const uint32_t va = vt + vlane[db];
-                const u32x2 r0 = lds_load_tr8<(64 * kk + 0) * ROWB>(va);
-                const u32x2 r1 = lds_load_tr8<(64 * kk + 16) * ROWB>(va);
-                const u32x2 r2 = lds_load_tr8<(64 * kk + 32) * ROWB>(va);
-                const u32x2 r3 = lds_load_tr8<(64 * kk + 48) * ROWB>(va);
-                const i32x8 a = __builtin_bit_cast(i32x8, (u32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]});
-                oacc[db] = mfma_f8(a, pf[kk], oacc[db]);
-            });
+        // O^T += V^T P'^T: op (kk, db) needs four transposing fetches; the fetches of PV_AHEAD
+        // later ops stay in flight ahead of each MFMA (a scheduling fence after every op keeps that)
+        constexpr int NPV = (BC / 64) * (D / 32), PV_AHEAD = 2;
+        auto pv_fetch = [&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value, kk = i / (D / 32), db = i % (D / 32);
+            const uint32_t va = vt + vo[db];
+            const u32x2 r0 = lds_load_tr8<(64 * kk + 0) * ROWB>(va);
+            const u32x2 r1 = lds_load_tr8<(64 * kk + 16) * ROWB>(va);
+            const u32x2 r2 = lds_load_tr8<(64 * kk + 32) * ROWB>(va);
+            const u32x2 r3 = lds_load_tr8<(64 * kk + 48) * ROWB>(va);
+            return __builtin_bit_cast(i32x8, (u32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]});
+        };
+        i32x8 ring[PV_AHEAD];
+        static_for<PV_AHEAD>([&](auto J) { ring[decltype(J)::value] = pv_fetch(J); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NPV>([&](auto J) {
+            constexpr int j = decltype(J)::value, kk = j / (D / 32), db = j % (D / 32);
+            const i32x8 a = ring[j % PV_AHEAD];
+            if constexpr (j + PV_AHEAD < NPV) ring[j % PV_AHEAD] = pv_fetch(std::integral_constant<int, j + PV_AHEAD>{});
+            oacc[db] = mfma_f8(a, pf[kk], oacc[db]);
+            __builtin_amdgcn_sched_barrier(0);
         });
         lrnd += rs[0] * ivd;
     };
