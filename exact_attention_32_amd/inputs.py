@@ -39,7 +39,7 @@ class Workload:
     S_q: int
     S_k: int
     d: int
-    dtype: str          # "f16", "bf16" or "fp8"
+    dtype: str          # "f16", "bf16", "fp8" (OCP E4M3) or "e5m2" (OCP E5M2)
     causal: bool
     seed: int
     outliers: bool = False
@@ -65,14 +65,19 @@ class Workload:
 
     def hbm_bytes(self) -> int:
         """Algorithmic HBM bytes: Q, K, V read once, O and LSE written once, descales read once."""
-        elt = 1 if self.dtype == "fp8" else 2
+        elt = 1 if is_fp8(self.dtype) else 2
         out_elt = 2
         n_q = self.B * self.H * self.S_q * self.d
         n_k = self.B * self.H * self.S_k * self.d
         total = n_q * elt + 2 * n_k * elt + n_q * out_elt + self.B * self.H * self.S_q * 4
-        if self.dtype == "fp8":
+        if is_fp8(self.dtype):
             total += 4 * self.B * self.H * (_nblk(self.S_q) + 2 * _nblk(self.S_k))
         return total
+
+
+def is_fp8(dtype: str) -> bool:
+    """Block-scaled 8-bit inputs: "fp8" (E4M3) or "e5m2"."""
+    return dtype in ("fp8", "e5m2")
 
 
 def _nblk(s: int) -> int:
@@ -137,8 +142,38 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return (code.astype(np.uint8) | sign).astype(np.uint8)
 
 
-def quantize_e4m3_blocks(x: np.ndarray, blk: int = FP8_BLOCK):
-    """Per-(b, h, blk-row block) scaling of x [B,H,S,d] fp32 -> (codes uint8, descale fp32 [B,H,nblk])."""
+E5M2_MAX = 57344.0
+
+
+def e5m2_encode(x: np.ndarray) -> np.ndarray:
+    """OCP E5M2 codes of float values: round-to-nearest-even, saturating to +-57344.
+
+    Format: sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent field 0
+    is subnormal (2^-14 * m/4); exponent field 31 holds inf / NaN, never produced here.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.minimum(np.abs(x), E5M2_MAX)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -14
+    code[sub] = np.rint(a[sub] * 2.0 ** 16).astype(np.int64)   # quantum 2^-16
+    nrm = ~sub
+    if np.any(nrm):
+        an = a[nrm]
+        _, e2 = np.frexp(an)
+        e = e2.astype(np.int64) - 1
+        mant = np.rint(an / np.ldexp(1.0, e) * 4.0).astype(np.int64) - 4   # 0..4
+        carry = mant == 4
+        e = np.where(carry, e + 1, e)
+        mant = np.where(carry, 0, mant)
+        c = ((e + 15) << 2) | mant
+        code[nrm] = np.minimum(c, 0x7B)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def quantize_fp8_blocks(x: np.ndarray, fmt: str = "e4m3", blk: int = FP8_BLOCK):
+    """Per-(b, h, blk-row block) scaling of x [B,H,S,d] fp32 to E4M3 or E5M2 codes -> (codes, descale [B,H,nblk])."""
+    enc, fmax = {"e4m3": (e4m3_encode, E4M3_MAX), "e5m2": (e5m2_encode, E5M2_MAX)}[fmt]
     B, H, S, d = x.shape
     nb = (S + blk - 1) // blk
     codes = np.empty(x.shape, dtype=np.uint8)
@@ -147,10 +182,15 @@ def quantize_e4m3_blocks(x: np.ndarray, blk: int = FP8_BLOCK):
         r0, r1 = j * blk, min(S, (j + 1) * blk)
         xb = x[:, :, r0:r1, :]
         amax = np.abs(xb).max(axis=(2, 3)).astype(np.float32)
-        ds = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        ds = np.where(amax > 0, amax / np.float32(fmax), np.float32(1.0)).astype(np.float32)
         desc[:, :, j] = ds
-        codes[:, :, r0:r1, :] = e4m3_encode(xb.astype(np.float64) / ds.astype(np.float64)[:, :, None, None])
+        codes[:, :, r0:r1, :] = enc(xb.astype(np.float64) / ds.astype(np.float64)[:, :, None, None])
     return codes, desc
+
+
+def quantize_e4m3_blocks(x: np.ndarray, blk: int = FP8_BLOCK):
+    """Per-(b, h, blk-row block) scaling of x [B,H,S,d] fp32 -> (codes uint8, descale fp32 [B,H,nblk])."""
+    return quantize_fp8_blocks(x, "e4m3", blk)
 
 
 _TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
@@ -167,10 +207,11 @@ def make_inputs(work: Workload) -> Inputs:
             n = int(0.01 * flat.size)
             idx = rng.choice(flat.size, size=n, replace=False)
             flat[idx] *= np.float32(10.0)
-    if work.dtype == "fp8":
-        qc, qd = quantize_e4m3_blocks(q)
-        kc, kd = quantize_e4m3_blocks(k)
-        vc, vd = quantize_e4m3_blocks(v)
+    if is_fp8(work.dtype):
+        fmt = "e5m2" if work.dtype == "e5m2" else "e4m3"
+        qc, qd = quantize_fp8_blocks(q, fmt)
+        kc, kd = quantize_fp8_blocks(k, fmt)
+        vc, vd = quantize_fp8_blocks(v, fmt)
         return Inputs(work, torch.from_numpy(qc), torch.from_numpy(kc), torch.from_numpy(vc),
                       torch.from_numpy(qd), torch.from_numpy(kd), torch.from_numpy(vd), q, k, v)
     dt = _TORCH_DT[work.dtype]

@@ -43,8 +43,9 @@
  *                            and the online forms agree.
  * plus oracle_decode_e4m3_blocks (fp8 input decoding, OCP E4M3 "fn" format
  * with per-(b, h, 128-row block) fp32 descale; the deep dive's section 4
- * block quantisation), oracle_quantize_e4m3_blocks (the block quantisation
- * itself: per-block |max|, descale, nearest code) and oracle_softmax_block
+ * block quantisation; oracle_decode_fp8_blocks also for OCP E5M2),
+ * oracle_quantize_fp8_blocks (the block quantisation itself: per-block |max|,
+ * descale, nearest code, E4M3 or E5M2) and oracle_softmax_block
  * (exposes one explicit P block so tests can check that softmax rows sum to
  * one).
  */
@@ -292,34 +293,60 @@ double oracle_e4m3_value(uint8_t code) {
     return s ? -mag : mag;
 }
 
+/*
+ * OCP 8-bit floating point, E5M2: 1 sign bit, 5 exponent bits with bias 15,
+ * 2 mantissa bits, IEEE-like specials.
+ *   e == 0            : (-1)^s * 2^-14 * (m / 4)        (subnormal)
+ *   e == 31, m == 0   : infinity;  e == 31, m != 0 : NaN
+ *   otherwise         : (-1)^s * 2^(e-15) * (1 + m / 4)  (max finite 57344)
+ */
+double oracle_e5m2_value(uint8_t code) {
+    const int s = code >> 7, e = (code >> 2) & 31, m = code & 3;
+    double mag;
+    if (e == 31) return m == 0 ? (s ? -INFINITY : INFINITY) : NAN;
+    if (e == 0) mag = ldexp((double)m / 4.0, -14);
+    else mag = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return s ? -mag : mag;
+}
+
+/* value of a code of format fmt (0: E4M3, 1: E5M2) */
+static double fp8_value(uint8_t code, int fmt) { return fmt ? oracle_e5m2_value(code) : oracle_e4m3_value(code); }
+
 /* x[b,h,r,:] = e4m3(codes[b,h,r,:]) * descale[b,h,r/blk] for a [B][H][S][d] tensor. */
-int oracle_decode_e4m3_blocks(const uint8_t *codes, const float *descale, int B, int H, int S, int d, int blk,
-                              double *out) {
-    if (!codes || !descale || !out || blk < 1) return -1;
+int oracle_decode_fp8_blocks(const uint8_t *codes, const float *descale, int B, int H, int S, int d, int blk,
+                             int fmt, double *out) {
+    if (!codes || !descale || !out || blk < 1 || fmt < 0 || fmt > 1) return -1;
     const int nblk = (S + blk - 1) / blk;
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
         for (int r = 0; r < S; ++r) {
             const double ds = (double)descale[bh * nblk + r / blk];
             for (int t = 0; t < d; ++t) {
                 const int64_t idx = (bh * S + r) * (int64_t)d + t;
-                out[idx] = oracle_e4m3_value(codes[idx]) * ds;
+                out[idx] = fp8_value(codes[idx], fmt) * ds;
             }
         }
     return 0;
 }
 
+int oracle_decode_e4m3_blocks(const uint8_t *codes, const float *descale, int B, int H, int S, int d, int blk,
+                              double *out) {
+    return oracle_decode_fp8_blocks(codes, descale, B, H, S, d, blk, 0, out);
+}
+
 /*
- * The finite E4M3 code nearest to the real value x, ties to the even code
- * (round to nearest even), found by scanning every finite non-negative code
- * (0x00 .. 0x7e).  Magnitudes above 448 get 448 (the nearest finite value),
- * i.e. the encoding saturates.  The sign bit is x's sign bit (-0 -> 0x80).
+ * The finite code of format fmt (0: E4M3, 1: E5M2) nearest to the real value
+ * x, ties to the even code (round to nearest even), found by scanning every
+ * finite non-negative code (E4M3 0x00 .. 0x7e, E5M2 0x00 .. 0x7b).
+ * Magnitudes above the largest finite value (448, 57344) get that value, i.e.
+ * the encoding saturates.  The sign bit is x's sign bit (-0 -> 0x80).
  */
-uint8_t oracle_e4m3_encode(double x) {
+uint8_t oracle_fp8_encode(double x, int fmt) {
     const double a = fabs(x);
+    const int top = fmt ? 0x7b : 0x7e;   /* largest finite code: 57344 (E5M2), 448 (E4M3) */
     int best = 0;
     double best_err = a;   /* code 0 has value 0 */
-    for (int c = 1; c <= 0x7e; ++c) {
-        const double err = fabs(oracle_e4m3_value((uint8_t)c) - a);
+    for (int c = 1; c <= top; ++c) {
+        const double err = fabs(fp8_value((uint8_t)c, fmt) - a);
         if (err < best_err || (err == best_err && (c & 1) == 0)) {
             best = c;
             best_err = err;
@@ -328,19 +355,23 @@ uint8_t oracle_e4m3_encode(double x) {
     return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
 }
 
+uint8_t oracle_e4m3_encode(double x) { return oracle_fp8_encode(x, 0); }
+
 /*
  * Block quantisation of a [B][H][S][d] fp32 tensor (the deep dive's section 4:
  * one scale per block from the block's local maximum): for each (b, h, block
  * of blk rows), amax = max |x| over the block (rows past S do not exist),
- * descale = amax / 448 as a float (448 = largest finite E4M3), or 1 when
- * amax = 0; code = oracle_e4m3_encode(x / descale).  The quotient is taken in
- * double: the exact quotient of two floats that is not exactly an E4M3
- * midpoint lies at least 2^-29 (relative) away from every midpoint, far
- * beyond the 2^-53 of the double rounding, so the code is that of the exact
- * quotient.
+ * descale = amax / fmax as a float (fmax = largest finite value: 448 for
+ * E4M3, 57344 for E5M2), or 1 when amax = 0; code = oracle_fp8_encode(
+ * x / descale, fmt).  The quotient is taken in double: the exact quotient of
+ * two floats that is not exactly a midpoint between codes lies at least 2^-29
+ * (relative) away from every midpoint, far beyond the 2^-53 of the double
+ * rounding, so the code is that of the exact quotient.
  */
-int oracle_quantize_e4m3_blocks(const float *x, int B, int H, int S, int d, int blk, uint8_t *codes, float *descale) {
-    if (!x || !codes || !descale || B < 1 || H < 1 || S < 1 || d < 1 || blk < 1) return -1;
+int oracle_quantize_fp8_blocks(const float *x, int B, int H, int S, int d, int blk, int fmt, uint8_t *codes,
+                               float *descale) {
+    if (!x || !codes || !descale || B < 1 || H < 1 || S < 1 || d < 1 || blk < 1 || fmt < 0 || fmt > 1) return -1;
+    const float fmax = fmt ? 57344.0f : 448.0f;   /* largest finite value of the format */
     const int nblk = (S + blk - 1) / blk;
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
         for (int j = 0; j < nblk; ++j) {
@@ -351,13 +382,17 @@ int oracle_quantize_e4m3_blocks(const float *x, int B, int H, int S, int d, int 
                     const float v = fabsf(x[(bh * S + r) * (int64_t)d + t]);
                     if (v > amax) amax = v;
                 }
-            const float ds = amax > 0.0f ? amax / 448.0f : 1.0f;
+            const float ds = amax > 0.0f ? amax / fmax : 1.0f;
             descale[bh * nblk + j] = ds;
             for (int r = r0; r < r1; ++r)
                 for (int t = 0; t < d; ++t) {
                     const int64_t idx = (bh * S + r) * (int64_t)d + t;
-                    codes[idx] = oracle_e4m3_encode((double)x[idx] / (double)ds);
+                    codes[idx] = oracle_fp8_encode((double)x[idx] / (double)ds, fmt);
                 }
         }
     return 0;
+}
+
+int oracle_quantize_e4m3_blocks(const float *x, int B, int H, int S, int d, int blk, uint8_t *codes, float *descale) {
+    return oracle_quantize_fp8_blocks(x, B, H, S, d, blk, 0, codes, descale);
 }

@@ -31,6 +31,7 @@ def build(src: str = SRC, out: str = LIB) -> str:
 
 
 _dptr = ctypes.POINTER(ctypes.c_double)
+_FMT = {"e4m3": 0, "e5m2": 1}
 
 
 def default_threads() -> int:
@@ -77,6 +78,14 @@ class Oracle:
         L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
         L.oracle_quantize_e4m3_blocks.restype = ci
         L.oracle_quantize_e4m3_blocks.argtypes = [ctypes.c_void_p] + [ci] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_e5m2_value.restype = cd
+        L.oracle_e5m2_value.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_encode.restype = ctypes.c_uint8
+        L.oracle_fp8_encode.argtypes = [ctypes.c_double, ci]
+        L.oracle_quantize_fp8_blocks.restype = ci
+        L.oracle_quantize_fp8_blocks.argtypes = [ctypes.c_void_p] + [ci] * 6 + [ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_decode_fp8_blocks.restype = ci
+        L.oracle_decode_fp8_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ci] * 6 + [_dptr]
         self.L = L
         self.last_threads = 0
 
@@ -159,6 +168,41 @@ class Oracle:
             raise ValueError("oracle rejected arguments")
         return out
 
+
+    def e5m2_table(self) -> np.ndarray:
+        """Value of each of the 256 OCP E5M2 codes (+-inf, NaN for the specials)."""
+        return np.array([self.L.oracle_e5m2_value(c) for c in range(256)], dtype=np.float64)
+
+    def fp8_encode(self, x, fmt: str) -> np.ndarray:
+        """Nearest finite code (ties to even, saturating) of format "e4m3" or "e5m2" for each value of x."""
+        f = _FMT[fmt]
+        x = np.asarray(x, dtype=np.float64)
+        return np.array([self.L.oracle_fp8_encode(float(v), f) for v in x.reshape(-1)], dtype=np.uint8).reshape(x.shape)
+
+    def quantize_fp8_blocks(self, x, fmt: str, blk: int = 128):
+        """Block quantisation of fp32 x [B,H,S,d] to "e4m3" / "e5m2" -> (codes, descale [B,H,ceil(S/blk)])."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+        B, H, S, d = x.shape
+        codes = np.empty(x.shape, np.uint8)
+        descale = np.empty((B, H, (S + blk - 1) // blk), np.float32)
+        r = self.L.oracle_quantize_fp8_blocks(x.ctypes.data, B, H, S, d, blk, _FMT[fmt], codes.ctypes.data,
+                                              descale.ctypes.data)
+        if r < 0:
+            raise ValueError("oracle rejected arguments")
+        return codes, descale
+
+    def decode_fp8_blocks(self, codes, descale, fmt: str, blk: int = 128) -> np.ndarray:
+        """Exact fp64 values of block-scaled "e4m3" / "e5m2" data."""
+        codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+        descale = np.ascontiguousarray(np.asarray(descale, dtype=np.float32))
+        B, H, S, d = codes.shape
+        if descale.shape != (B, H, (S + blk - 1) // blk):
+            raise ValueError("descale shape must be [B, H, ceil(S/blk)]")
+        out = np.empty(codes.shape, np.float64)
+        r = self.L.oracle_decode_fp8_blocks(codes.ctypes.data, descale.ctypes.data, B, H, S, d, blk, _FMT[fmt], _p(out))
+        if r < 0:
+            raise ValueError("oracle rejected arguments")
+        return out
 
     def e4m3_encode(self, x) -> np.ndarray:
         """Nearest finite E4M3 code (ties to even, saturating) of each value of x (any shape)."""

@@ -343,6 +343,40 @@ def check_quantize_blocks(oracle):
     assert np.all(codes[1, 2, 0:128] == 0) and ds[1, 2, 0] == 1.0
 
 
+def check_e5m2(oracle):
+    """E5M2 values against torch's float8_e5m2 view of all 256 codes; nearest-even encoding against
+    torch's cast on finite values, midpoints and their neighbouring floats; saturation at 57344;
+    block quantisation against the input generator's E5M2 quantiser."""
+    from exact_attention_32_amd import inputs as I
+
+    table = oracle.e5m2_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(table), nan) and np.array_equal(table[~nan], ref[~nan])
+    vals = ref[:0x7C]                                   # 0 .. 57344, code order
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    rng = np.random.Generator(np.random.PCG64(1500))
+    pos = np.concatenate([vals.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf)),
+                          np.nextafter(mids, np.float32(0)), np.exp2(rng.uniform(-18, 15.8, 3000)).astype(np.float32)])
+    pos = pos[pos <= 57344]
+    x = np.concatenate([pos, -pos]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    got = oracle.fp8_encode(x.astype(np.float64), "e5m2")
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(want[i])) for i in bad[:5]]
+    big = np.array([57345.0, 61439.0, 61440.0, 1e6])
+    assert np.all(oracle.fp8_encode(big, "e5m2") == 0x7B) and np.all(oracle.fp8_encode(-big, "e5m2") == 0xFB)
+    xq = rng.standard_normal((2, 2, 200, 8), dtype=np.float32)
+    xq[:, :, 128:] *= np.float32(1e-3)
+    c, d = oracle.quantize_fp8_blocks(xq, "e5m2")
+    rc, rd = I.quantize_fp8_blocks(xq, "e5m2")
+    assert np.array_equal(c, rc) and np.array_equal(d, rd)
+    amax = np.abs(xq[:, :, :128]).max(axis=(2, 3)).astype(np.float32)
+    assert np.array_equal(d[:, :, 0], (amax / np.float32(57344.0)).astype(np.float32))
+    dec = oracle.decode_fp8_blocks(c, d, "e5m2")
+    assert np.array_equal(dec, table[c] * np.repeat(d.astype(np.float64), 128, axis=2)[:, :, :200, None])
+
+
 ALL_CHECKS = [
     check_sdpa_fp64,
     check_lse_logsumexp,
@@ -357,6 +391,7 @@ ALL_CHECKS = [
     check_e4m3_decode,
     check_e4m3_encode,
     check_quantize_blocks,
+    check_e5m2,
     check_decode_blocks,
     check_large_scores,
 ]

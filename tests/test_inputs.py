@@ -77,3 +77,33 @@ def test_workload_accounting(name):
     w = I.WORKLOADS[name]
     n = w.S_q * (w.S_q + 1) // 2 if w.causal else w.S_q * w.S_k
     assert w.flops() == 4 * w.d * n * w.B * w.H
+
+
+def test_e5m2_encoder_matches_torch_cast_in_range():
+    rng = np.random.Generator(np.random.PCG64(12))
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * 3000,
+        rng.uniform(-57344, 57344, 100000).astype(np.float32),
+        np.exp2(rng.uniform(-20, 15.8, 100000)).astype(np.float32),
+    ])
+    x = x[np.abs(x) <= 57344]
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(I.e5m2_encode(x), ref)
+
+
+def test_e5m2_encoder_saturates():
+    big = np.array([57344.0, 57345.0, 61439.0, 61440.0, 1e9])
+    assert np.all(I.e5m2_encode(big) == 0x7B) and np.all(I.e5m2_encode(-big) == 0xFB)
+
+
+def test_e5m2_block_quantisation():
+    w = I.random_workload(1, 2, 260, 260, 64, "e5m2", False, seed=6)
+    x = I.make_inputs(w)
+    tab = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    for codes, ds, raw in ((x.q, x.q_descale, x.q32), (x.k, x.k_descale, x.k32)):
+        assert ds.shape == (1, 2, 3)
+        dec = tab[codes.numpy()] * np.repeat(ds.numpy().astype(np.float64), 128, axis=2)[:, :, :260, None]
+        # 2 mantissa bits: relative error at most 2^-3 for normal codes
+        assert np.all(np.abs(dec - raw) <= np.abs(raw) * 2.0 ** -3 + 2.0 ** -16 * ds.numpy().max())
+        amax = np.abs(raw[:, :, :128]).max(axis=(2, 3)).astype(np.float32)
+        assert np.array_equal(ds.numpy()[:, :, 0], amax / np.float32(57344.0))

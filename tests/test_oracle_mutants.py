@@ -35,12 +35,15 @@ MUTANTS = {
     "e4m3_sign": ("return s ? -mag : mag;", "return mag;"),
     "descale_block_index": ("descale[bh * nblk + r / blk]", "descale[bh * nblk + (r + 1) / blk]"),
     "e4m3_ties_to_odd": ("(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
-    "e4m3_scan_short": ("for (int c = 1; c <= 0x7e; ++c) {", "for (int c = 1; c <= 0x77; ++c) {"),
+    "e4m3_scan_short": ("const int top = fmt ? 0x7b : 0x7e;", "const int top = fmt ? 0x7b : 0x77;"),
     "e4m3_sign_dropped": ("return (uint8_t)(best | (signbit(x) ? 0x80 : 0));", "return (uint8_t)best;"),
-    "quant_descale_240": ("const float ds = amax > 0.0f ? amax / 448.0f : 1.0f;",
-                          "const float ds = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    "quant_descale_240": ("const float fmax = fmt ? 57344.0f : 448.0f;", "const float fmax = fmt ? 57344.0f : 240.0f;"),
     "quant_block_short": ("const int r0 = j * blk, r1 = (r0 + blk < S) ? r0 + blk : S;",
                           "const int r0 = j * blk, r1 = (r0 + blk < S) ? r0 + blk - 1 : S;"),
+    "e5m2_bias": ("else mag = ldexp(1.0 + (double)m / 4.0, e - 15);", "else mag = ldexp(1.0 + (double)m / 4.0, e - 16);"),
+    "e5m2_subnormal": ("if (e == 0) mag = ldexp((double)m / 4.0, -14);", "if (e == 0) mag = ldexp((double)m / 4.0, -15);"),
+    "e5m2_top_code": ("const int top = fmt ? 0x7b : 0x7e;", "const int top = fmt ? 0x7a : 0x7e;"),
+    "e5m2_fmax": ("const float fmax = fmt ? 57344.0f : 448.0f;", "const float fmax = fmt ? 49152.0f : 448.0f;"),
     "quant_amax_signed": ("const float v = fabsf(x[(bh * S + r) * (int64_t)d + t]);",
                           "const float v = x[(bh * S + r) * (int64_t)d + t];"),
 }
