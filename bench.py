@@ -28,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "bf16_b2_h16_s4096_d128"
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "e5m2": 5000.0}
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_32_amd", "csrc", "attn_fwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -61,17 +61,19 @@ def run_gpu(work, x, steps: int, warmup: int):
     import torch
 
     import exact_attention_32_amd as ea
+    from exact_attention_32_amd import inputs as I
 
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     o = torch.empty((work.B, work.H, work.S_q, work.d), device=dev,
                     dtype=torch.float16 if work.dtype == "f16" else torch.bfloat16)
     lse = torch.empty((work.B, work.H, work.S_q), device=dev, dtype=torch.float32)
-    if work.dtype == "fp8":
+    if I.is_fp8(work.dtype):
         qd, kd, vd = x.q_descale.to(dev), x.k_descale.to(dev), x.v_descale.to(dev)
+        fmt = "e5m2" if work.dtype == "e5m2" else "e4m3"
 
         def step():
-            ea.fwd_fp8(q, k, v, qd, kd, vd, causal=work.causal, scale=work.scale, out=o, lse=lse)
+            ea.fwd_fp8(q, k, v, qd, kd, vd, causal=work.causal, scale=work.scale, out=o, lse=lse, fmt=fmt)
     else:
         def step():
             ea.fwd(q, k, v, causal=work.causal, scale=work.scale, out=o, lse=lse)
@@ -163,7 +165,7 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": counter_traffic(work.name),
-            "kernel": "attn_fwd_fp8_kernel" if work.dtype == "fp8" else "attn_fwd_kernel",
+            "kernel": "attn_fwd_fp8_kernel" if I.is_fp8(work.dtype) else "attn_fwd_kernel",
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
             "min_launch_us": round(float(np.min(per_launch)) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,
@@ -287,10 +289,12 @@ def run_cpu_baseline(work, x, target_s: float):
 
 
 def _oracle_arrays(work, x, orc):
-    if work.dtype == "fp8":
-        return (orc.decode_e4m3_blocks(x.q.numpy(), x.q_descale.numpy()),
-                orc.decode_e4m3_blocks(x.k.numpy(), x.k_descale.numpy()),
-                orc.decode_e4m3_blocks(x.v.numpy(), x.v_descale.numpy()))
+    from exact_attention_32_amd import inputs as I
+
+    if I.is_fp8(work.dtype):
+        fmt = "e5m2" if work.dtype == "e5m2" else "e4m3"
+        return tuple(orc.decode_fp8_blocks(c.numpy(), ds.numpy(), fmt)
+                     for c, ds in ((x.q, x.q_descale), (x.k, x.k_descale), (x.v, x.v_descale)))
     return x.q.double().numpy(), x.k.double().numpy(), x.v.double().numpy()
 
 

@@ -15,7 +15,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 
-ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3, ATTN_F32 = 0, 1, 2, 3
+ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3, ATTN_F32, ATTN_FP8_E5M2 = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -38,12 +38,16 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     L.attn_fwd_fp8.restype = ci
     L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
+    L.attn_fwd_fp8_e5m2.restype = ci
+    L.attn_fwd_fp8_e5m2.argtypes = L.attn_fwd_fp8.argtypes
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_status_string.argtypes = [ci]
     L.attn_fwd_plan.restype = ci
     L.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci] + [ctypes.POINTER(ci)] * 4
     L.attn_quantize_e4m3.restype = ci
     L.attn_quantize_e4m3.argtypes = [vp, ci, vp, vp, ci, ci, ci, ci, vp]
+    L.attn_quantize_e5m2.restype = ci
+    L.attn_quantize_e5m2.argtypes = L.attn_quantize_e4m3.argtypes
     if path == LIB_PATH:
         _lib = L
     return L
@@ -111,13 +115,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     return out, lse
 
 
+_FP8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
 def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scale: float | None = None,
-            out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
-    """Block-scaled fp8 (OCP E4M3 codes, uint8 or float8_e4m3fn) attention -> (O bf16, LSE fp32)."""
+            out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True,
+            fmt: str = "e4m3"):
+    """Block-scaled fp8 attention -> (O bf16, LSE fp32).
+
+    q, k, v hold OCP codes of the format ``fmt`` ("e4m3" or "e5m2") as uint8 or as the matching
+    torch float8 dtype; descales are fp32 [B, H, ceil(S/128)].
+    """
+    if fmt not in _FP8_TORCH:
+        raise ValueError(f"fmt must be 'e4m3' or 'e5m2', not {fmt!r}")
     B, H, S_q, S_k, d = _shapes(q, k, v)
     for t in (q, k, v):
-        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
-            raise ValueError("fp8 inputs must be uint8 codes or float8_e4m3fn")
+        if t.dtype not in (torch.uint8, _FP8_TORCH[fmt]):
+            raise ValueError(f"fp8 inputs must be uint8 codes or {_FP8_TORCH[fmt]}")
     for t, s in ((q_descale, S_q), (k_descale, S_k), (v_descale, S_k)):
         if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (B, H, (s + 127) // 128):
             raise ValueError("descales must be contiguous fp32 device tensors [B, H, ceil(S/128)]")
@@ -127,19 +141,24 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scal
         out = torch.empty((B, H, S_q, d), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
-    rc = load_library().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(),
-                                     k_descale.data_ptr(), v_descale.data_ptr(), out.data_ptr(),
-                                     lse.data_ptr() if lse is not None else None, B, H, S_q, S_k, d,
-                                     int(bool(causal)), float(scale), _stream(q.device))
+    L = load_library()
+    entry = L.attn_fwd_fp8 if fmt == "e4m3" else L.attn_fwd_fp8_e5m2
+    rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
+               v_descale.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, S_q, S_k,
+               d, int(bool(causal)), float(scale), _stream(q.device))
     _check(rc)
     return out, lse
 
 
-def quantize_e4m3(x: torch.Tensor, codes: torch.Tensor | None = None, descale: torch.Tensor | None = None):
-    """Per-(b, h, 128-row block) E4M3 quantisation of x [B, H, S, d] (fp32, bf16 or fp16) on the GPU.
+def quantize_fp8(x: torch.Tensor, fmt: str = "e4m3", codes: torch.Tensor | None = None,
+                 descale: torch.Tensor | None = None):
+    """Per-(b, h, 128-row block) fp8 quantisation of x [B, H, S, d] (fp32, bf16 or fp16) on the GPU.
 
-    Returns (codes uint8 [B, H, S, d], descale fp32 [B, H, ceil(S/128)]), the inputs of fwd_fp8.
+    fmt is "e4m3" or "e5m2".  Returns (codes uint8 [B, H, S, d], descale fp32 [B, H, ceil(S/128)]),
+    the inputs of fwd_fp8 with the same fmt.
     """
+    if fmt not in _FP8_TORCH:
+        raise ValueError(f"fmt must be 'e4m3' or 'e5m2', not {fmt!r}")
     if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous [B, H, S, d] device tensor")
     dt = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(x.dtype)
@@ -154,7 +173,18 @@ def quantize_e4m3(x: torch.Tensor, codes: torch.Tensor | None = None, descale: t
         raise ValueError("codes must be a contiguous uint8 tensor of x's shape")
     if tuple(descale.shape) != (B, H, (S + 127) // 128) or descale.dtype != torch.float32 or not descale.is_contiguous():
         raise ValueError("descale must be a contiguous fp32 tensor [B, H, ceil(S/128)]")
-    rc = load_library().attn_quantize_e4m3(x.data_ptr(), dt, codes.data_ptr(), descale.data_ptr(), B, H, S, d,
-                                           _stream(x.device))
+    L = load_library()
+    entry = L.attn_quantize_e4m3 if fmt == "e4m3" else L.attn_quantize_e5m2
+    rc = entry(x.data_ptr(), dt, codes.data_ptr(), descale.data_ptr(), B, H, S, d, _stream(x.device))
     _check(rc)
     return codes, descale
+
+
+def quantize_e4m3(x: torch.Tensor, codes: torch.Tensor | None = None, descale: torch.Tensor | None = None):
+    """quantize_fp8 with fmt="e4m3"."""
+    return quantize_fp8(x, "e4m3", codes, descale)
+
+
+def quantize_e5m2(x: torch.Tensor, codes: torch.Tensor | None = None, descale: torch.Tensor | None = None):
+    """quantize_fp8 with fmt="e5m2"."""
+    return quantize_fp8(x, "e5m2", codes, descale)

@@ -798,15 +798,20 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
 // Block-scaled fp8 path (the FlashAttention-3 deep dive (techknowgenie), section 4: per-block
 // scale factors, both products in FP8, softmax and accumulation in FP32).
 //
-// Q, K, V hold OCP E4M3 codes; the value of row r of a head is code * descale[r / 128].  One key
+// Q, K, V hold OCP fp8 codes, all three E4M3 or all three E5M2 (the template argument FMT; the
+// deep dive's section 4 names both formats); the value of row r of a head is
+// code * descale[r / 128].  One key
 // tile is one descale block (128 keys).  With raw = Q_code . K_code (exact in the fp32 MFMA
 // accumulator), the base-2 score is raw * c_t with c_t = scale * log2(e) * qd * kd_t.  V's
 // descale enters as a per-tile bias of the exponent: the kernel keeps the running max m of
 // raw * c_t + log2(vd_t) and forms p' = exp2(raw * c_t + log2(vd_t) - m) = vd_t * p, so that
 // sum_j p'_j * Vcode_j = sum_j p_j * V_j with no per-tile rescale of O; the row sums take p'
-// times 1 / vd_t.  p' <= 2^RESCALE_LOG2 = 256 fits E4M3 (largest finite 448).
+// times 1 / vd_t.  p' <= 2^RESCALE_LOG2 = 256 fits E4M3 (largest finite 448), and P' is rounded
+// to E4M3 for either input format: the matrix core takes a different format for each operand,
+// and E4M3 keeps one more mantissa bit of the probabilities than E5M2 would.
 //
-// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales).  It sums A[i][k] B[k][j] over
+// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales; operand format 0 = E4M3,
+// 1 = E5M2).  It sums A[i][k] B[k][j] over
 // the pairs (lane half, byte) that A and B share, so any key order that both operands use is
 // valid.  The order used here is the one of the S^T accumulator: byte b of lane half g of
 // k-step kk is key 64 kk + 32 (b / 16) + 8 ((b % 16) / 4) + 4 g + b % 4, so P^T is packed
@@ -829,9 +834,10 @@ struct ParamsF8 {
     float c;                     // scale * log2(e)
 };
 
+// operand formats FA (of A) and FB (of B): 0 = E4M3, 1 = E5M2; block scale exponents 127 (2^0)
+template <int FA, int FB>
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
-    // format 0 (E4M3) for A and B, block scale exponents 127 (2^0)
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
 }
 
 // four floats -> four E4M3 bytes (round to nearest even), first value in the low byte
@@ -853,7 +859,7 @@ template <int OFF> __device__ __forceinline__ u32x2 lds_load_tr8(uint32_t addr) 
     return __builtin_bit_cast(u32x2, v);
 }
 
-template <int D, int NS, bool CAUSAL>
+template <int D, int NS, bool CAUSAL, int FMT>
 __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
     constexpr int NW = 8, BC = 128, BR = NW * 32;
     constexpr int ROWB = D;              // bytes per K/V row
@@ -972,7 +978,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
                 const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(kt + ko[2 * ks]);
                 const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(kt + ko[2 * ks + 1]);
                 const i32x8 a = __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                s[kb2] = mfma_f8(a, qf[ks], s[kb2]);
+                s[kb2] = mfma_f8<FMT, FMT>(a, qf[ks], s[kb2]);
             });
         });
         if (masked) {
@@ -1033,7 +1039,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
         // sum of the rounded p' (the weights P.V uses): ones x P'^T on the matrix core
         f32x16 rs = {};
 #pragma unroll
-        for (int kk = 0; kk < BC / 64; ++kk) rs = mfma_f8(ones, pf[kk], rs);
+        for (int kk = 0; kk < BC / 64; ++kk) rs = mfma_f8<0, 0>(ones, pf[kk], rs);
         // O^T += V^T P'^T: op (kk, db) needs four transposing fetches; the fetches of PV_AHEAD
         // later ops stay in flight ahead of each MFMA (a scheduling fence after every op keeps that)
         constexpr int NPV = (BC / 64) * (D / 32), PV_AHEAD = 2;
@@ -1053,7 +1059,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             constexpr int j = decltype(J)::value, kk = j / (D / 32), db = j % (D / 32);
             const i32x8 a = ring[j % PV_AHEAD];
             if constexpr (j + PV_AHEAD < NPV) ring[j % PV_AHEAD] = pv_fetch(std::integral_constant<int, j + PV_AHEAD>{});
-            oacc[db] = mfma_f8(a, pf[kk], oacc[db]);
+            oacc[db] = mfma_f8<FMT, 0>(a, pf[kk], oacc[db]);
             __builtin_amdgcn_sched_barrier(0);
         });
         lrnd += rs[0] * ivd;
@@ -1222,15 +1228,22 @@ void make_plan_fp8(int B, int H, int Sq, Plan *pl) {
     if (wg <= INT_MAX) pl->num_wg = (int)wg;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 int launch_fp8(const ParamsF8 &p, const Plan &pl, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, kFp8Stages, CAUSAL>), dim3(pl.num_wg), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, kFp8Stages, CAUSAL, FMT>), dim3(pl.num_wg), dim3(512), 0, s, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+template <int FMT>
+int launch_fp8_d(const ParamsF8 &p, const Plan &pl, int d, int causal, hipStream_t s) {
+    if (d == 128) return causal ? launch_fp8<128, true, FMT>(p, pl, s) : launch_fp8<128, false, FMT>(p, pl, s);
+    return causal ? launch_fp8<64, true, FMT>(p, pl, s) : launch_fp8<64, false, FMT>(p, pl, s);
+}
+
+// fmt: 0 = E4M3 codes, 1 = E5M2 codes
 int run_fp8(const void *q, const void *k, const void *v, const float *q_descale, const float *k_descale,
             const float *v_descale, void *o, float *lse, int B, int H, int S_q, int S_k, int d, int causal,
-            float scale, void *stream) {
+            float scale, int fmt, void *stream) {
     Plan pl;
     make_plan_fp8(B, H, S_q, &pl);
     if (pl.num_wg == 0) return ATTN_ERR_OVERFLOW;
@@ -1252,8 +1265,15 @@ int run_fp8(const void *q, const void *k, const void *v, const float *q_descale,
     p.xcd_remap = (pl.num_wg % 8 == 0) ? 1 : 0;
     p.c = scale * 1.44269504088896340736f;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (d == 128) return causal ? launch_fp8<128, true>(p, pl, s) : launch_fp8<128, false>(p, pl, s);
-    return causal ? launch_fp8<64, true>(p, pl, s) : launch_fp8<64, false>(p, pl, s);
+    return fmt ? launch_fp8_d<1>(p, pl, d, causal, s) : launch_fp8_d<0>(p, pl, d, causal, s);
+}
+
+int check_descales(const float *q_descale, const float *k_descale, const float *v_descale) {
+    if (!q_descale || !k_descale || !v_descale) return ATTN_ERR_DESCALE;
+    if ((reinterpret_cast<uintptr_t>(q_descale) | reinterpret_cast<uintptr_t>(k_descale) |
+         reinterpret_cast<uintptr_t>(v_descale)) & 3u)
+        return ATTN_ERR_DESCALE;
+    return ATTN_OK;
 }
 
 }  // namespace
@@ -1262,8 +1282,9 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
                         int S_k, int d, int causal, float scale, int dtype, void *stream) {
     int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
     if (st != ATTN_OK) return st;
-    if (dtype == ATTN_FP8_E4M3)
-        return run_fp8(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, S_q, S_k, d, causal, scale, stream);
+    if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2)
+        return run_fp8(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, S_q, S_k, d, causal, scale,
+                       dtype == ATTN_FP8_E5M2 ? 1 : 0, stream);
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     Plan pl;
     st = make_plan(B, H, S_q, d, causal, &pl);
@@ -1290,20 +1311,29 @@ extern "C" int attn_fwd_fp8(const void *q, const void *k, const void *v, const f
                             int S_q, int S_k, int d, int causal, float scale, void *stream) {
     int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
     if (st != ATTN_OK) return st;
-    if (!q_descale || !k_descale || !v_descale) return ATTN_ERR_DESCALE;
-    if ((reinterpret_cast<uintptr_t>(q_descale) | reinterpret_cast<uintptr_t>(k_descale) |
-         reinterpret_cast<uintptr_t>(v_descale)) & 3u)
-        return ATTN_ERR_DESCALE;
-    return run_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, S_q, S_k, d, causal, scale, stream);
+    st = check_descales(q_descale, k_descale, v_descale);
+    if (st != ATTN_OK) return st;
+    return run_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, S_q, S_k, d, causal, scale, 0, stream);
+}
+
+extern "C" int attn_fwd_fp8_e5m2(const void *q, const void *k, const void *v, const float *q_descale,
+                                 const float *k_descale, const float *v_descale, void *o, float *lse, int B, int H,
+                                 int S_q, int S_k, int d, int causal, float scale, void *stream) {
+    int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
+    if (st != ATTN_OK) return st;
+    st = check_descales(q_descale, k_descale, v_descale);
+    if (st != ATTN_OK) return st;
+    return run_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, S_q, S_k, d, causal, scale, 1, stream);
 }
 
 extern "C" int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, int dtype, int *block_q,
                              int *block_k, int *waves, int *workgroups) {
     if (B < 1 || H < 1 || S_q < 1 || S_k < 1) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-    if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3 && dtype != ATTN_FP8_E5M2)
+        return ATTN_ERR_UNSUPPORTED;
     Plan pl;
-    if (dtype == ATTN_FP8_E4M3) {
+    if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2) {
         make_plan_fp8(B, H, S_q, &pl);
         if (pl.num_wg == 0) return ATTN_ERR_OVERFLOW;
     } else {

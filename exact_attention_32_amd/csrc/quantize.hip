@@ -1,10 +1,11 @@
-// quantize.hip -- per-block E4M3 quantisation on MI355X (gfx950).
+// quantize.hip -- per-block fp8 (E4M3 or E5M2) quantisation on MI355X (gfx950).
 //
 // The step before the block-scaled fp8 attention: one fp32 scale per
 // (batch, head, 128-row block) taken from the block's largest |x|
 // (FlashAttention-3 deep dive (techknowgenie), section 4, block quantisation),
-// descale = amax / 448 (448 = largest finite E4M3; 1 for an all-zero block),
-// code = the E4M3 value nearest to x / descale, ties to even, saturating.
+// descale = amax / fmax (fmax = largest finite value: 448 for E4M3, 57344 for
+// E5M2; 1 for an all-zero block), code = the fp8 value nearest to
+// x / descale, ties to even, saturating at +-fmax.
 //
 // The path is HBM-bound (4, 2 or 2 bytes in and 1 byte out per element), so the
 // kernel is one read of the block into registers, one reduction, one write:
@@ -58,19 +59,32 @@ template <> __device__ __forceinline__ f32x4 load4<f16_t>(const f16_t *p) {
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
+// Format constants: largest finite value, smallest normal, the float mantissa bits below the
+// kept ones (mask and the midpoint pattern), and 1 / half the subnormal spacing.
+template <int FMT> struct Fp8Fmt;
+template <> struct Fp8Fmt<0> {   // E4M3: 3 mantissa bits, subnormal spacing 2^-9
+    static constexpr float fmax = 448.0f, min_normal = 0x1p-6f, inv_half_ulp_sub = 1024.0f;
+    static constexpr uint32_t low_mask = 0xFFFFFu, half = 0x80000u;
+};
+template <> struct Fp8Fmt<1> {   // E5M2: 2 mantissa bits, subnormal spacing 2^-16
+    static constexpr float fmax = 57344.0f, min_normal = 0x1p-14f, inv_half_ulp_sub = 131072.0f;
+    static constexpr uint32_t low_mask = 0x1FFFFFu, half = 0x100000u;
+};
+
 // x / ds as the float that the hardware's nearest-even conversion maps to the code of the exact
-// quotient (see the file comment); |result| <= 448
-__device__ __forceinline__ float quotient(float x, float ds) {
+// quotient (see the file comment); |result| <= fmax
+template <int FMT> __device__ __forceinline__ float quotient(float x, float ds) {
+    using F = Fp8Fmt<FMT>;
     float q = x / ds;   // correctly rounded division
     const float a = fabsf(q);
-    if (a >= 448.0f) return copysignf(448.0f, q);
+    if (a >= F::fmax) return copysignf(F::fmax, q);
     bool mid;
-    if (a >= 0x1p-6f) {
-        // normal E4M3 range: 3 mantissa bits kept, the next one set, the rest zero
-        mid = (__float_as_uint(a) & 0xFFFFFu) == 0x80000u;
+    if (a >= F::min_normal) {
+        // normal range: the kept mantissa bits, the next one set, the rest zero
+        mid = (__float_as_uint(a) & F::low_mask) == F::half;
     } else {
-        // subnormal E4M3 range: midpoints are the odd multiples of 2^-10
-        const float t = a * 1024.0f;
+        // subnormal range: midpoints are the odd multiples of half the spacing
+        const float t = a * F::inv_half_ulp_sub;
         mid = (t == truncf(t)) && (((int)t & 1) != 0);
     }
     if (mid) {
@@ -87,9 +101,20 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-template <int D, class In>
-__global__ __launch_bounds__(QTHREADS) void quantize_e4m3_kernel(const In *__restrict__ x, uint32_t *__restrict__ codes,
-                                                                 float *__restrict__ descale, int S, int nblk) {
+// four quotients -> four codes (nearest even), first value in the low byte
+template <int FMT> __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d);
+template <> __device__ __forceinline__ uint32_t pack4<0>(float a, float b, float c, float d) {
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+template <> __device__ __forceinline__ uint32_t pack4<1>(float a, float b, float c, float d) {
+    const int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+}
+
+template <int D, class In, int FMT>
+__global__ __launch_bounds__(QTHREADS) void quantize_fp8_kernel(const In *__restrict__ x, uint32_t *__restrict__ codes,
+                                                                float *__restrict__ descale, int S, int nblk) {
     constexpr int PER = QBLK * D / 4 / QTHREADS;   // groups of 4 elements per thread
     static_assert(PER * 4 * QTHREADS == QBLK * D, "block shape");
     const int tid = threadIdx.x;
@@ -116,38 +141,35 @@ __global__ __launch_bounds__(QTHREADS) void quantize_e4m3_kernel(const In *__res
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float ds = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float ds = amax > 0.0f ? amax / Fp8Fmt<FMT>::fmax : 1.0f;
     if (tid == 0) descale[blk] = ds;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
         const int g = tid + p * QTHREADS;
         if ((4 * g) / D < rows) {
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(v[p][0], ds), quotient(v[p][1], ds), 0, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(quotient(v[p][2], ds), quotient(v[p][3], ds), w, true);
-            codes[(base + 4 * g) / 4] = (uint32_t)w;
+            codes[(base + 4 * g) / 4] = pack4<FMT>(quotient<FMT>(v[p][0], ds), quotient<FMT>(v[p][1], ds),
+                                                   quotient<FMT>(v[p][2], ds), quotient<FMT>(v[p][3], ds));
         }
     }
 }
 
-template <int D>
+template <int D, int FMT>
 int launch_quant(const void *x, int dtype, void *codes, float *descale, int nwg, int S, int nblk, hipStream_t s) {
     uint32_t *c = static_cast<uint32_t *>(codes);
     if (dtype == ATTN_F32)
-        hipLaunchKernelGGL((quantize_e4m3_kernel<D, float>), dim3(nwg), dim3(QTHREADS), 0, s,
+        hipLaunchKernelGGL((quantize_fp8_kernel<D, float, FMT>), dim3(nwg), dim3(QTHREADS), 0, s,
                            static_cast<const float *>(x), c, descale, S, nblk);
     else if (dtype == ATTN_BF16)
-        hipLaunchKernelGGL((quantize_e4m3_kernel<D, bf16_t>), dim3(nwg), dim3(QTHREADS), 0, s,
+        hipLaunchKernelGGL((quantize_fp8_kernel<D, bf16_t, FMT>), dim3(nwg), dim3(QTHREADS), 0, s,
                            static_cast<const bf16_t *>(x), c, descale, S, nblk);
     else
-        hipLaunchKernelGGL((quantize_e4m3_kernel<D, f16_t>), dim3(nwg), dim3(QTHREADS), 0, s,
+        hipLaunchKernelGGL((quantize_fp8_kernel<D, f16_t, FMT>), dim3(nwg), dim3(QTHREADS), 0, s,
                            static_cast<const f16_t *>(x), c, descale, S, nblk);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
-                                  void *stream) {
+template <int FMT>
+int quantize(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d, void *stream) {
     if (!x || !codes) return ATTN_ERR_NULL;
     if (!descale) return ATTN_ERR_DESCALE;
     if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
@@ -159,6 +181,18 @@ extern "C" int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *
     const long long nwg = (long long)B * H * nblk;
     if (nwg > INT_MAX || (long long)B * H > INT_MAX / S) return ATTN_ERR_OVERFLOW;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (d == 128) return launch_quant<128>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
-    return launch_quant<64>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
+    if (d == 128) return launch_quant<128, FMT>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
+    return launch_quant<64, FMT>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
+}
+
+}  // namespace
+
+extern "C" int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
+                                  void *stream) {
+    return quantize<0>(x, dtype, codes, descale, B, H, S, d, stream);
+}
+
+extern "C" int attn_quantize_e5m2(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
+                                  void *stream) {
+    return quantize<1>(x, dtype, codes, descale, B, H, S, d, stream);
 }

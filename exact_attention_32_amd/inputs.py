@@ -94,6 +94,7 @@ WORKLOADS = {
         Workload("fp8_b2_h16_s4096_d128", 2, 16, 4096, 4096, 128, "fp8", False, 4),
         Workload("bf16_causal_outliers_b1_h16_s16384_d64", 1, 16, 16384, 16384, 64, "bf16", True, 5, True),
         Workload("bf16_b2_h16_s4096_d128", 2, 16, 4096, 4096, 128, "bf16", False, 6),
+        Workload("e5m2_b2_h16_s4096_d128", 2, 16, 4096, 4096, 128, "e5m2", False, 7),
     ]
 }
 

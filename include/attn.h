@@ -38,7 +38,8 @@ typedef enum {
     ATTN_F16 = 0,       /* q, k, v, o are IEEE binary16 */
     ATTN_BF16 = 1,      /* q, k, v, o are bfloat16 */
     ATTN_FP8_E4M3 = 2,  /* q, k, v are OCP E4M3 codes (unit descales), o is bfloat16 */
-    ATTN_F32 = 3        /* IEEE binary32: an input type of attn_quantize_e4m3 only */
+    ATTN_F32 = 3,       /* IEEE binary32: an input type of the quantisers only */
+    ATTN_FP8_E5M2 = 4   /* q, k, v are OCP E5M2 codes (unit descales), o is bfloat16 */
 } attn_dtype;
 
 typedef enum {
@@ -83,6 +84,17 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v, const float *q_des
                  float scale, void *stream);
 
 /*
+ * As attn_fwd_fp8 for OCP E5M2 codes (the deep dive's section 4 names E5M2
+ * beside E4M3: two mantissa bits, a range up to 57344): the real value of
+ * element [b,h,r,t] is e5m2(code) * descale[b,h,r/128].  The probabilities
+ * are still rounded to E4M3 for the P.V product.  Arguments, layout, errors
+ * and ownership as for attn_fwd_fp8.
+ */
+int attn_fwd_fp8_e5m2(const void *q, const void *k, const void *v, const float *q_descale,
+                      const float *k_descale, const float *v_descale, void *o, float *lse, int B, int H, int S_q,
+                      int S_k, int d, int causal, float scale, void *stream);
+
+/*
  * Block quantisation to OCP E4M3, the input preparation of attn_fwd_fp8 (the
  * FlashAttention-3 deep dive, section 4: one scale per block, from the block's
  * largest magnitude).  For every (b, h) and block of 128 rows of
@@ -99,6 +111,15 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v, const float *q_des
  * Returns an attn_status (ATTN_ERR_DESCALE for a NULL or misaligned descale).
  */
 int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
+                       void *stream);
+
+/*
+ * Block quantisation to OCP E5M2, the input preparation of attn_fwd_fp8_e5m2:
+ * as attn_quantize_e4m3 with 57344 (the largest finite E5M2) in place of 448,
+ * and the E5M2 code nearest to x / descale (ties to even, saturating at
+ * +-57344).  Arguments, layout, errors and ownership as for attn_quantize_e4m3.
+ */
+int attn_quantize_e5m2(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
                        void *stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */

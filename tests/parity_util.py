@@ -7,10 +7,10 @@ import torch
 from exact_attention_32_amd import inputs as I
 
 # Tolerances (max abs error against the fp64 oracle).
-TOL_O = {"f16": 1e-2, "bf16": 1e-2, "fp8": 5e-2}
+TOL_O = {"f16": 1e-2, "bf16": 1e-2, "fp8": 5e-2, "e5m2": 5e-2}
 TOL_LSE = 1e-3
 
-_OUT_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.bfloat16}
+_OUT_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.bfloat16, "e5m2": torch.bfloat16}
 
 
 def say(msg: str):
@@ -19,10 +19,10 @@ def say(msg: str):
 
 def oracle_inputs(x: I.Inputs, oracle):
     """Exact fp64 values of the inputs (fp8: decoded codes times descales)."""
-    if x.work.dtype == "fp8":
-        return (oracle.decode_e4m3_blocks(x.q.numpy(), x.q_descale.numpy()),
-                oracle.decode_e4m3_blocks(x.k.numpy(), x.k_descale.numpy()),
-                oracle.decode_e4m3_blocks(x.v.numpy(), x.v_descale.numpy()))
+    if I.is_fp8(x.work.dtype):
+        fmt = "e5m2" if x.work.dtype == "e5m2" else "e4m3"
+        return tuple(oracle.decode_fp8_blocks(c.numpy(), ds.numpy(), fmt)
+                     for c, ds in ((x.q, x.q_descale), (x.k, x.k_descale), (x.v, x.v_descale)))
     return x.q.double().numpy(), x.k.double().numpy(), x.v.double().numpy()
 
 
@@ -30,9 +30,10 @@ def run_gpu(x: I.Inputs, dev="cuda:0"):
     import exact_attention_32_amd as ea
 
     w = x.work
-    if w.dtype == "fp8":
+    if I.is_fp8(w.dtype):
         o, lse = ea.fwd_fp8(x.q.to(dev), x.k.to(dev), x.v.to(dev), x.q_descale.to(dev), x.k_descale.to(dev),
-                            x.v_descale.to(dev), causal=w.causal, scale=w.scale)
+                            x.v_descale.to(dev), causal=w.causal, scale=w.scale,
+                            fmt="e5m2" if w.dtype == "e5m2" else "e4m3")
     else:
         o, lse = ea.fwd(x.q.to(dev), x.k.to(dev), x.v.to(dev), causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()

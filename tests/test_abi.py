@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_fwd_plan", "attn_quantize_e4m3"}
+    assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e5m2", "attn_status_string", "attn_fwd_plan",
+                          "attn_quantize_e4m3", "attn_quantize_e5m2"}
     for n in names:
         assert hasattr(lib, n), f"library does not export {n}"
 
@@ -48,8 +49,14 @@ def call(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Sq=16, Sk=16, d=128, causal=0
     return lib.attn_fwd(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, None)
 
 
+FP8_ENTRIES = ("attn_fwd_fp8", "attn_fwd_fp8_e5m2")
+
+
 def call8(lib, q=P, k=P, v=P, qd=P, kd=P, vd=P, o=P, lse=P, B=1, H=1, Sq=16, Sk=16, d=128, causal=0, scale=0.125):
-    return lib.attn_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, H, Sq, Sk, d, causal, scale, None)
+    """Both fp8 entry points must return the same status; that status."""
+    rcs = {getattr(lib, n)(q, k, v, qd, kd, vd, o, lse, B, H, Sq, Sk, d, causal, scale, None) for n in FP8_ENTRIES}
+    assert len(rcs) == 1, rcs
+    return rcs.pop()
 
 
 def test_null_pointers(lib):
@@ -102,8 +109,9 @@ def test_plan(lib):
     with pytest.raises(ea.AttnError):
         ea.plan(1, 1, 16, 16, 96)
     # fp8: one 128-key tile per descale block
-    bq, bk, w, n = ea.plan(2, 16, 4096, 4096, 128, False, dtype=ea.ATTN_FP8_E4M3)
-    assert bk == 128 and bq % 128 == 0 and n == -(-4096 // bq) * 32
+    for dt in (ea.ATTN_FP8_E4M3, ea.ATTN_FP8_E5M2):
+        bq, bk, w, n = ea.plan(2, 16, 4096, 4096, 128, False, dtype=dt)
+        assert bk == 128 and bq % 128 == 0 and n == -(-4096 // bq) * 32
 
 
 def test_binding_rejects_host_tensors():
@@ -115,7 +123,10 @@ def test_binding_rejects_host_tensors():
 
 
 def callq(lib, x=P, dtype=3, codes=P, ds=P, B=1, H=1, S=16, d=128):
-    return lib.attn_quantize_e4m3(x, dtype, codes, ds, B, H, S, d, None)
+    """Both quantisers must return the same status; that status."""
+    rcs = {getattr(lib, n)(x, dtype, codes, ds, B, H, S, d, None) for n in ("attn_quantize_e4m3", "attn_quantize_e5m2")}
+    assert len(rcs) == 1, rcs
+    return rcs.pop()
 
 
 def test_quantize_validation(lib):
@@ -123,6 +134,7 @@ def test_quantize_validation(lib):
     assert callq(lib, ds=None) == DESCALE and callq(lib, ds=P + 2) == DESCALE
     for kw in ("B", "H", "S"):
         assert callq(lib, **{kw: 0}) == SHAPE
-    assert callq(lib, d=96) == UNSUP and callq(lib, dtype=2) == UNSUP and callq(lib, dtype=7) == UNSUP
+    assert callq(lib, d=96) == UNSUP and callq(lib, dtype=2) == UNSUP and callq(lib, dtype=4) == UNSUP
+    assert callq(lib, dtype=7) == UNSUP
     assert callq(lib, x=P + 4) == ALIGN and callq(lib, codes=P + 8) == ALIGN
     assert callq(lib, B=2 ** 16, H=2 ** 16, S=2 ** 10) == OVERFLOW

@@ -1,7 +1,7 @@
 """GPU parity: the HIP kernels against the fp64 oracle, element by element.
 
-Gate (spec tolerances): max |O - O_ref| <= 1e-2 for f16/bf16 and 5e-2 for
-fp8, measured on top of each element's own output rounding
+Gate: max |O - O_ref| <= 1e-2 for f16/bf16 and 5e-2 for fp8 (E4M3 and E5M2),
+measured on top of each element's own output rounding
 (|round(O_ref) - O_ref|, which alone can exceed 1e-2 where |O| >= 4 in bf16);
 max |LSE - LSE_ref| <= 1e-3.
 """
@@ -68,6 +68,15 @@ def test_small_full(oracle, shape, dtype, causal):
 def test_small_full_fp8(oracle, shape, causal):
     B, H, Sq, Sk, d = shape
     w = I.random_workload(B, H, Sq, Sk, d, "fp8", causal, seed=2000 + Sq + 7 * Sk + d)
+    st = _run_full(oracle, w)
+    assert st["pass"], st
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_full_e5m2(oracle, shape, causal):
+    B, H, Sq, Sk, d = shape
+    w = I.random_workload(B, H, Sq, Sk, d, "e5m2", causal, seed=2500 + Sq + 7 * Sk + d)
     st = _run_full(oracle, w)
     assert st["pass"], st
 

@@ -1,4 +1,4 @@
-"""GPU parity of the per-block E4M3 quantiser: bit-exact against the oracle's quantiser.
+"""GPU parity of the per-block fp8 (E4M3, E5M2) quantisers: bit-exact against the oracle's quantiser.
 
 Codes and descales are integer / exactly specified outputs, so the bar is
 equality: fp32 inputs are compared with the oracle run on the same fp32
@@ -35,14 +35,14 @@ def _draw(shape, seed, spread=True):
     return x
 
 
-def _check(oracle, x32: np.ndarray, dtype: torch.dtype):
+def _check(oracle, x32: np.ndarray, dtype: torch.dtype, fmt: str = "e4m3"):
     import exact_attention_32_amd as ea
 
     xt = torch.from_numpy(x32).to(dtype)
     exact32 = xt.float().numpy()          # the exact values the kernel sees
-    codes, ds = ea.quantize_e4m3(xt.to("cuda:0"))
+    codes, ds = ea.quantize_fp8(xt.to("cuda:0"), fmt)
     torch.cuda.synchronize()
-    rc, rd = oracle.quantize_e4m3_blocks(exact32)
+    rc, rd = oracle.quantize_fp8_blocks(exact32, fmt)
     gc, gd = codes.cpu().numpy(), ds.cpu().numpy()
     assert np.array_equal(gd, rd), np.argwhere(gd != rd)[:5]
     bad = np.argwhere(gc != rc)
@@ -52,44 +52,51 @@ def _check(oracle, x32: np.ndarray, dtype: torch.dtype):
 SHAPES = [(1, 1, 1, 64), (1, 2, 127, 128), (2, 3, 300, 64), (1, 2, 513, 128), (2, 2, 1024, 128)]
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16], ids=["f32", "bf16", "f16"])
-def test_quantize_matches_oracle(oracle, shape, dtype):
+def test_quantize_matches_oracle(oracle, shape, dtype, fmt):
     x = _draw(shape, 3000 + sum(shape))
     if dtype == torch.float16:
         x = np.clip(x, -6e4, 6e4)
-    U.say(f"[gpu] quantize {shape} {dtype}")
-    _check(oracle, x, dtype)
+    U.say(f"[gpu] quantize {fmt} {shape} {dtype}")
+    _check(oracle, x, dtype, fmt)
 
 
-def test_quantize_special_blocks(oracle):
-    """All-zero block (descale 1), negative zero, exact E4M3 midpoints after scaling, saturation edge."""
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quantize_special_blocks(oracle, fmt):
+    """All-zero block (descale 1), negative zero, exact midpoints of the code grid after scaling
+    (normal and subnormal), saturation edge."""
     x = np.zeros((1, 1, 384, 64), np.float32)
-    # block 1: values that are exact midpoints of the scaled grid (amax = 448 -> descale 1)
-    tab = torch.arange(128, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()[:127]
+    # block 1: values that are exact midpoints of the scaled grid (amax = fmax -> descale 1)
+    tdt, ncode, fmax = ((torch.float8_e4m3fn, 127, 448.0) if fmt == "e4m3" else (torch.float8_e5m2, 124, 57344.0))
+    tab = torch.arange(ncode, dtype=torch.uint8).view(tdt).to(torch.float64).numpy()
     mids = ((tab[:-1] + tab[1:]) / 2).astype(np.float32)
     blk = x[0, 0, 128:256].reshape(-1)
     blk[:mids.size] = mids
     blk[mids.size:2 * mids.size] = -mids
-    blk[-1] = 448.0
+    blk[-1] = fmax
     # block 2: -0.0 entries and values around the largest code
     b2 = x[0, 0, 256:384].reshape(-1)
     b2[:] = np.float32(-0.0)
     b2[0:4] = [1.0, -1.0, 0.999, 1.0001]
-    U.say("[gpu] quantize special blocks")
-    _check(oracle, x, torch.float32)
+    U.say(f"[gpu] quantize special blocks {fmt}")
+    _check(oracle, x, torch.float32, fmt)
 
 
-def test_quantized_inputs_drive_fp8_attention(oracle):
-    """quantize_e4m3 -> fwd_fp8 reproduces the fp8 path of the input generator (same codes)."""
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quantized_inputs_drive_fp8_attention(oracle, fmt):
+    """quantize_fp8 -> fwd_fp8 reproduces the fp8 path of the input generator (same codes)."""
     import exact_attention_32_amd as ea
     from exact_attention_32_amd import inputs as I
 
-    w = I.random_workload(1, 2, 200, 200, 128, "fp8", False, seed=77)
+    w = I.random_workload(1, 2, 200, 200, 128, "fp8" if fmt == "e4m3" else "e5m2", False, seed=77)
     x = I.make_inputs(w)
     dev = "cuda:0"
-    qc, qd = ea.quantize_e4m3(torch.from_numpy(x.q32).to(dev))
+    U.say(f"[gpu] quantize -> fwd_fp8 {fmt}")
+    qc, qd = ea.quantize_fp8(torch.from_numpy(x.q32).to(dev), fmt)
     assert torch.equal(qc.cpu(), x.q) and torch.equal(qd.cpu(), x.q_descale)
-    o1, l1 = ea.fwd_fp8(qc, x.k.to(dev), x.v.to(dev), qd, x.k_descale.to(dev), x.v_descale.to(dev), scale=w.scale)
+    o1, l1 = ea.fwd_fp8(qc, x.k.to(dev), x.v.to(dev), qd, x.k_descale.to(dev), x.v_descale.to(dev), scale=w.scale,
+                        fmt=fmt)
     o2, l2 = U.run_gpu(x)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
