@@ -38,9 +38,10 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counter_traffic(workload: str):
-    """HBM bytes per launch from the committed PMC summary, if taken on this kernel source."""
-    path = os.path.join(PROFILES, f"attn_fwd_{workload}_pmc.txt")
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary of this kernel and workload, if taken on
+    this kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -142,6 +143,10 @@ def main(argv=None):
     avg_launch_ms = float(np.mean(per_launch))
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[work.dtype]
+    import exact_attention_32_amd as ea
+
+    dt_code = {"bf16": ea.ATTN_BF16, "f16": ea.ATTN_F16, "fp8": ea.ATTN_FP8_E4M3, "e5m2": ea.ATTN_FP8_E5M2}[work.dtype]
+    kernel = ea.kernel_name(work.d, work.causal, dt_code)
 
     result = {
         "metric": "attention fwd TFLOP/s and % of MI355X peak MFMA (bf16, fp8)",
@@ -164,8 +169,8 @@ def main(argv=None):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": counter_traffic(work.name),
-            "kernel": "attn_fwd_fp8_kernel" if I.is_fp8(work.dtype) else "attn_fwd_kernel",
+            "traffic": counter_traffic(kernel, work.name),
+            "kernel": kernel,
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
             "min_launch_us": round(float(np.min(per_launch)) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,

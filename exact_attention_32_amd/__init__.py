@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 
 ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3, ATTN_F32, ATTN_FP8_E5M2 = 0, 1, 2, 3, 4
+ATTN_SCHED_DEFAULT, ATTN_SCHED_CLASSIC, ATTN_SCHED_PINGPONG, ATTN_SCHED_DEPHASED = 0, 1, 2, 3
 
 _lib = None
 
@@ -48,6 +49,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.attn_quantize_e4m3.argtypes = [vp, ci, vp, vp, ci, ci, ci, ci, vp]
     L.attn_quantize_e5m2.restype = ci
     L.attn_quantize_e5m2.argtypes = L.attn_quantize_e4m3.argtypes
+    L.attn_fwd_set_policy.restype = ci
+    L.attn_fwd_set_policy.argtypes = [ci, ci, ci, ci]
+    L.attn_fwd_schedule.restype = ci
+    L.attn_fwd_schedule.argtypes = [ci, ci, ci]
     if path == LIB_PATH:
         _lib = L
     return L
@@ -67,6 +72,26 @@ def plan(B, H, S_q, S_k, d, causal=False, dtype=ATTN_BF16):
     out = [ctypes.c_int() for _ in range(4)]
     _check(load_library().attn_fwd_plan(B, H, S_q, S_k, d, int(bool(causal)), dtype, *[ctypes.byref(x) for x in out]))
     return tuple(x.value for x in out)
+
+
+def set_policy(schedule: int = ATTN_SCHED_DEFAULT, qb: int = 1, nw: int = 8, ns: int = 4):
+    """Process-wide choice of the f16/bf16 schedule and tile shape (tuning and tests);
+    ATTN_SCHED_DEFAULT restores the measured policy table."""
+    _check(load_library().attn_fwd_set_policy(int(schedule), int(qb), int(nw), int(ns)))
+
+
+KERNEL_NAMES = {ATTN_SCHED_CLASSIC: "attn_fwd_kernel", ATTN_SCHED_PINGPONG: "attn_fwd_pp_kernel",
+                ATTN_SCHED_DEPHASED: "attn_fwd_dp_kernel"}
+
+
+def kernel_name(d: int, causal: bool, dtype: int) -> str:
+    """Name of the HIP kernel that fwd / fwd_fp8 launch for these arguments under the current policy."""
+    if dtype in (ATTN_FP8_E4M3, ATTN_FP8_E5M2):
+        return "attn_fwd_fp8_kernel"
+    r = load_library().attn_fwd_schedule(int(d), int(bool(causal)), int(dtype))
+    if r < 0:
+        _check(-r)
+    return KERNEL_NAMES[r]
 
 
 def _shapes(q, k, v):

@@ -122,6 +122,36 @@ int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *descale, in
 int attn_quantize_e5m2(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
                        void *stream);
 
+/* Schedules of the f16/bf16 kernel (attn_fwd_set_policy). */
+typedef enum {
+    ATTN_SCHED_DEFAULT = 0,   /* the library's measured policy table */
+    ATTN_SCHED_CLASSIC = 1,   /* all waves: S = QK^T, softmax, O += PV per tile */
+    ATTN_SCHED_PINGPONG = 2,  /* wave groups alternate barrier-separated MFMA and softmax intervals */
+    ATTN_SCHED_DEPHASED = 3   /* the SIMD partner waves run one softmax behind */
+} attn_schedule;
+
+/*
+ * Tuning and test hook: makes every later f16/bf16 attn_fwd call of this
+ * process use one compiled schedule and tile shape (qb 32-query blocks per
+ * wave, nw waves per workgroup, ns LDS stages) instead of the measured policy
+ * table.  Compiled: CLASSIC (1,8,3) (1,8,4) (2,4,3) (2,4,4) (1,4,2) (1,4,3),
+ * PINGPONG (1,8,3), DEPHASED (1,8,4).  schedule = ATTN_SCHED_DEFAULT restores
+ * the table (the other arguments are then ignored).  The environment variable
+ * ATTN_FWD_POLICY="schedule,qb,nw,ns", read at the first call, sets the same
+ * override.  Process-wide, not tied to a stream: calls in flight keep the
+ * shape they were launched with.  Returns ATTN_OK, or ATTN_ERR_UNSUPPORTED
+ * for a shape that is not compiled (the setting is then unchanged).
+ */
+int attn_fwd_set_policy(int schedule, int qb, int nw, int ns);
+
+/*
+ * The schedule that attn_fwd launches for head dimension d, causal flag and
+ * dtype under the current policy (for reports and profiles): an attn_schedule
+ * value for ATTN_F16 / ATTN_BF16; ATTN_SCHED_DEFAULT (0) for the fp8 dtypes,
+ * which have one kernel; minus an attn_status for bad arguments.
+ */
+int attn_fwd_schedule(int d, int causal, int dtype);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char *attn_status_string(int status);
 

@@ -33,7 +33,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e5m2", "attn_status_string", "attn_fwd_plan",
-                          "attn_quantize_e4m3", "attn_quantize_e5m2"}
+                          "attn_quantize_e4m3", "attn_quantize_e5m2", "attn_fwd_set_policy"}
     for n in names:
         assert hasattr(lib, n), f"library does not export {n}"
 
@@ -138,3 +138,24 @@ def test_quantize_validation(lib):
     assert callq(lib, dtype=7) == UNSUP
     assert callq(lib, x=P + 4) == ALIGN and callq(lib, codes=P + 8) == ALIGN
     assert callq(lib, B=2 ** 16, H=2 ** 16, S=2 ** 10) == OVERFLOW
+
+
+COMPILED = [(ea.ATTN_SCHED_CLASSIC, 1, 8, 3), (ea.ATTN_SCHED_CLASSIC, 1, 8, 4), (ea.ATTN_SCHED_CLASSIC, 2, 4, 3),
+            (ea.ATTN_SCHED_CLASSIC, 2, 4, 4), (ea.ATTN_SCHED_CLASSIC, 1, 4, 2), (ea.ATTN_SCHED_CLASSIC, 1, 4, 3),
+            (ea.ATTN_SCHED_PINGPONG, 1, 8, 3), (ea.ATTN_SCHED_DEPHASED, 1, 8, 4)]
+
+
+def test_set_policy(lib):
+    try:
+        for bad in ((ea.ATTN_SCHED_CLASSIC, 3, 8, 4), (ea.ATTN_SCHED_PINGPONG, 1, 8, 4), (9, 1, 8, 4),
+                    (ea.ATTN_SCHED_DEPHASED, 1, 8, 3)):
+            assert lib.attn_fwd_set_policy(*bad) == UNSUP
+        for sched, qb, nw, ns in COMPILED:
+            assert lib.attn_fwd_set_policy(sched, qb, nw, ns) == OK
+            bq, bk, w, n = ea.plan(2, 16, 4096, 4096, 128, False)
+            assert (bq, bk, w) == (qb * nw * 32, 64, nw) and n == -(-4096 // bq) * 32
+            # fp8 plans do not follow the f16/bf16 override
+            assert ea.plan(2, 16, 4096, 4096, 128, False, dtype=ea.ATTN_FP8_E4M3)[:3] == (256, 128, 8)
+    finally:
+        assert lib.attn_fwd_set_policy(ea.ATTN_SCHED_DEFAULT, 0, 0, 0) == OK
+    assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 64, 8)

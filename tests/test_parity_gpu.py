@@ -81,6 +81,30 @@ def test_small_full_e5m2(oracle, shape, causal):
     assert st["pass"], st
 
 
+SCHEDULES = [(1, 1, 8, 3), (1, 1, 8, 4), (1, 2, 4, 3), (1, 2, 4, 4), (1, 1, 4, 2), (1, 1, 4, 3), (2, 1, 8, 3),
+             (3, 1, 8, 4)]
+SCHED_SHAPES = [(1, 1, 1, 1, 64), (1, 2, 17, 3, 128), (2, 3, 130, 130, 64), (1, 2, 300, 333, 128),
+                (1, 2, 513, 257, 128), (1, 2, 1000, 1000, 64)]
+
+
+@pytest.mark.parametrize("sched", SCHEDULES, ids=lambda s: "s%d_%d_%d_%d" % s)
+def test_every_schedule(oracle, sched):
+    """Every compiled schedule and tile shape (not only the policy table's choice), bf16 and f16,
+    causal and not, on ragged shapes at both head dimensions."""
+    import exact_attention_32_amd as ea
+
+    ea.set_policy(*sched)
+    try:
+        for i, (B, H, Sq, Sk, d) in enumerate(SCHED_SHAPES):
+            for dtype in ("bf16", "f16"):
+                for causal in (False, True):
+                    w = I.random_workload(B, H, Sq, Sk, d, dtype, causal, seed=3000 + 17 * i + sched[0])
+                    st = _run_full(oracle, w)
+                    assert st["pass"], (sched, w.name, st)
+    finally:
+        ea.set_policy(ea.ATTN_SCHED_DEFAULT)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_outliers_small(oracle, causal):
     w = I.random_workload(1, 2, 700, 700, 64, "bf16", causal, seed=55, outliers=True)
