@@ -45,7 +45,9 @@
  * with per-(b, h, 128-row block) fp32 descale; the deep dive's section 4
  * block quantisation; oracle_decode_fp8_blocks also for OCP E5M2),
  * oracle_quantize_fp8_blocks (the block quantisation itself: per-block |max|,
- * descale, nearest code, E4M3 or E5M2) and oracle_softmax_block
+ * descale, nearest code, E4M3 or E5M2), oracle_rmsnorm_across_heads (the
+ * QK-RMSNorm that precedes attention in the sglang QKNorm-across-heads
+ * write-up: one RMS per token over all heads) and oracle_softmax_block
  * (exposes one explicit P block so tests can check that softmax rows sum to
  * one).
  */
@@ -395,4 +397,37 @@ int oracle_quantize_fp8_blocks(const float *x, int B, int H, int S, int d, int b
 
 int oracle_quantize_e4m3_blocks(const float *x, int B, int H, int S, int d, int blk, uint8_t *codes, float *descale) {
     return oracle_quantize_fp8_blocks(x, B, H, S, d, blk, 0, codes, descale);
+}
+
+/*
+ * RMSNorm across heads (sglang QKNorm-across-heads write-up (blog.secrett2633),
+ * its key-code section: one reduction per token over the whole hidden vector,
+ * then rsqrt(eps + sum of squares / hidden size), times a per-channel weight).
+ * The hidden vector of token (b, s) is the H*d values x[b][h][s][t] of all
+ * heads h; hidden channel h*d + t has weight w[h*d + t]:
+ *
+ *   ms         = (1 / (H*d)) * sum_{h,t} x[b][h][s][t]^2
+ *   out[b][h][s][t] = x[b][h][s][t] / sqrt(eps + ms) * w[h*d + t]
+ *
+ * x, out: [B][H][S][d] fp64 (may alias); w: [H*d] fp64.  All fp64.
+ */
+int oracle_rmsnorm_across_heads(const double *x, const double *w, int B, int H, int S, int d, double eps,
+                                double *out) {
+    if (!x || !w || !out || B < 1 || H < 1 || S < 1 || d < 1 || !(eps >= 0.0)) return -1;
+    const int64_t hs = (int64_t)S * d;   /* stride between heads of one token */
+    for (int b = 0; b < B; ++b)
+        for (int s = 0; s < S; ++s) {
+            const int64_t base = (int64_t)b * H * hs + (int64_t)s * d;
+            double ss = 0.0;
+            for (int h = 0; h < H; ++h)
+                for (int t = 0; t < d; ++t) {
+                    const double v = x[base + h * hs + t];
+                    ss += v * v;
+                }
+            const double ms = ss / ((double)H * d);
+            const double r = 1.0 / sqrt(eps + ms);
+            for (int h = 0; h < H; ++h)
+                for (int t = 0; t < d; ++t) out[base + h * hs + t] = x[base + h * hs + t] * r * w[h * d + t];
+        }
+    return 0;
 }

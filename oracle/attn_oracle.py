@@ -86,6 +86,8 @@ class Oracle:
         L.oracle_quantize_fp8_blocks.argtypes = [ctypes.c_void_p] + [ci] * 6 + [ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_decode_fp8_blocks.restype = ci
         L.oracle_decode_fp8_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ci] * 6 + [_dptr]
+        L.oracle_rmsnorm_across_heads.restype = ci
+        L.oracle_rmsnorm_across_heads.argtypes = [_dptr, _dptr] + [ci] * 4 + [cd, _dptr]
         self.L = L
         self.last_threads = 0
 
@@ -201,6 +203,18 @@ class Oracle:
         out = np.empty(codes.shape, np.float64)
         r = self.L.oracle_decode_fp8_blocks(codes.ctypes.data, descale.ctypes.data, B, H, S, d, blk, _FMT[fmt], _p(out))
         if r < 0:
+            raise ValueError("oracle rejected arguments")
+        return out
+
+    def rmsnorm_across_heads(self, x, w, eps: float) -> np.ndarray:
+        """fp64 RMSNorm of every token's hidden vector (all heads) of x [B,H,S,d], weight w [H*d]."""
+        x = _f64(x)
+        w = _f64(w).reshape(-1)
+        B, H, S, d = x.shape
+        if w.size != H * d:
+            raise ValueError("w must have H*d entries")
+        out = np.empty_like(x)
+        if self.L.oracle_rmsnorm_across_heads(_p(x), _p(w), B, H, S, d, float(eps), _p(out)) < 0:
             raise ValueError("oracle rejected arguments")
         return out
 

@@ -377,6 +377,59 @@ def check_e5m2(oracle):
     assert np.array_equal(dec, table[c] * np.repeat(d.astype(np.float64), 128, axis=2)[:, :, :200, None])
 
 
+def check_rmsnorm(oracle):
+    """RMSNorm across heads against closed forms and invariants: a constant token gives
+    c / sqrt(eps + c^2) * w; with eps = 0 and unit weights every token's hidden vector (all heads)
+    has mean square 1, the ratio between heads of one token is kept (one RMS per token, not per
+    head), the map is invariant under positive scaling and odd; a one-hot weight selects exactly
+    its channel (h * d + t); tokens are independent; an all-zero token stays zero."""
+    rng = np.random.Generator(np.random.PCG64(4100))
+    B, H, S, d = 2, 3, 5, 4
+    # constant tokens: closed form
+    for c, eps in ((0.5, 0.0), (0.5, 1e-6), (-3.0, 0.25), (1e-4, 1e-6)):
+        x = np.full((B, H, S, d), c)
+        w = rng.uniform(0.5, 2.0, H * d)
+        out = oracle.rmsnorm_across_heads(x, w, eps)
+        want = c / math.sqrt(eps + c * c) * w.reshape(1, H, 1, d)
+        assert np.allclose(out, np.broadcast_to(want, out.shape), rtol=1e-14, atol=0)
+    # unit mean square per token over all heads; heads of different scale keep their ratio
+    x = rng.standard_normal((B, H, S, d))
+    x[:, 1] *= 10.0
+    x[:, 2] *= 0.01
+    ones = np.ones(H * d)
+    out = oracle.rmsnorm_across_heads(x, ones, 0.0)
+    ms = (out ** 2).mean(axis=(1, 3))
+    assert np.allclose(ms, 1.0, rtol=0, atol=1e-12)
+    ratio = out / x
+    assert np.allclose(ratio, ratio[:, :1, :, :1], rtol=1e-13, atol=0)
+    # positive scaling invariance and oddness (eps = 0)
+    assert np.allclose(oracle.rmsnorm_across_heads(3.7 * x, ones, 0.0), out, rtol=1e-13, atol=0)
+    assert np.array_equal(oracle.rmsnorm_across_heads(-x, ones, 0.0), -out)
+    # one-hot weight: only channel (h, t) survives, with the token's factor
+    for h, t in ((0, 0), (2, 3), (1, 2)):
+        w = np.zeros(H * d)
+        w[h * d + t] = 1.0
+        o1 = oracle.rmsnorm_across_heads(x, w, 0.0)
+        mask = np.zeros((H, d), bool)
+        mask[h, t] = True
+        assert np.all(o1.transpose(0, 2, 1, 3)[:, :, ~mask] == 0.0)
+        assert np.allclose(o1[:, h, :, t], out[:, h, :, t], rtol=1e-14, atol=0)
+    # tokens are independent; a zero token stays zero (eps > 0)
+    x2 = x.copy()
+    x2[1, :, 3, :] = 0.0
+    x2[0, :, 2, :] *= 5.0
+    o2 = oracle.rmsnorm_across_heads(x2, ones, 1e-6)
+    o_ref = oracle.rmsnorm_across_heads(x, ones, 1e-6)
+    keep = np.ones((B, S), bool)
+    keep[1, 3] = keep[0, 2] = False
+    assert np.array_equal(o2.transpose(0, 2, 1, 3)[keep], o_ref.transpose(0, 2, 1, 3)[keep])
+    assert np.all(o2[1, :, 3, :] == 0.0)
+    # eps enters under the square root, added to the mean square
+    xs = np.full((1, 2, 1, 2), 1e-3)
+    o3 = oracle.rmsnorm_across_heads(xs, np.ones(4), 1e-6)
+    assert np.allclose(o3, 1e-3 / math.sqrt(1e-6 + 1e-6), rtol=1e-14, atol=0)
+
+
 ALL_CHECKS = [
     check_sdpa_fp64,
     check_lse_logsumexp,
@@ -392,6 +445,7 @@ ALL_CHECKS = [
     check_e4m3_encode,
     check_quantize_blocks,
     check_e5m2,
+    check_rmsnorm,
     check_decode_blocks,
     check_large_scores,
 ]

@@ -44,6 +44,12 @@ MUTANTS = {
     "e5m2_subnormal": ("if (e == 0) mag = ldexp((double)m / 4.0, -14);", "if (e == 0) mag = ldexp((double)m / 4.0, -15);"),
     "e5m2_top_code": ("const int top = fmt ? 0x7b : 0x7e;", "const int top = fmt ? 0x7a : 0x7e;"),
     "e5m2_fmax": ("const float fmax = fmt ? 57344.0f : 448.0f;", "const float fmax = fmt ? 49152.0f : 448.0f;"),
+    "rms_eps_outside": ("const double r = 1.0 / sqrt(eps + ms);", "const double r = 1.0 / sqrt(ms) + eps;"),
+    "rms_sum_not_mean": ("const double ms = ss / ((double)H * d);", "const double ms = ss / (double)d;"),
+    "rms_weight_index": ("* r * w[h * d + t];", "* r * w[t];"),
+    "rms_per_head": ("            double ss = 0.0;\n            for (int h = 0; h < H; ++h)",
+                     "            double ss = 0.0;\n            for (int h = 0; h < 1; ++h)"),
+    "rms_no_inverse": ("const double r = 1.0 / sqrt(eps + ms);", "const double r = sqrt(eps + ms);"),
     "quant_amax_signed": ("const float v = fabsf(x[(bh * S + r) * (int64_t)d + t]);",
                           "const float v = x[(bh * S + r) * (int64_t)d + t];"),
 }
