@@ -110,6 +110,9 @@ def main(argv=None):
     ap.add_argument("--quantize", action="store_true",
                     help="instead of the attention benchmark, time the per-block E4M3 quantiser on the fp32 Q, K, V "
                          "of the fp8 workload (HBM-bound; reports GB/s)")
+    ap.add_argument("--qknorm", action="store_true",
+                    help="instead of the attention benchmark, time the QK-RMSNorm across heads on the Q and K of "
+                         "the bf16 workload (HBM-bound; reports GB/s)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -125,6 +128,8 @@ def main(argv=None):
         return copy_calibration(args.copy_calibration, max(1, args.steps))
     if args.quantize:
         return bench_quantize(args.steps, args.warmup, not args.no_cpu_baseline)
+    if args.qknorm:
+        return bench_qknorm(args.steps, args.warmup, not args.no_cpu_baseline)
 
     import numpy as np
 
@@ -259,6 +264,75 @@ def bench_quantize(steps: int, warmup: int, cpu: bool) -> int:
         dt = time.perf_counter() - t1
         result["cpu_baseline"] = {"value": round(a.size * 5 / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                                   "sample": f"2 of 32 (b,h) heads of Q ({a.size} elements), single-threaded; {dt:.2f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_qknorm(steps: int, warmup: int, cpu: bool) -> int:
+    """One step = RMSNorm across heads of the bf16 Q and K of the bench's default workload (one launch)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_32_amd as ea
+    from exact_attention_32_amd import inputs as I
+
+    work = I.WORKLOADS[DEFAULT_WORKLOAD]
+    x = I.make_inputs(work)
+    dev = torch.device("cuda:0")
+    q, k = x.q.to(dev), x.k.to(dev)
+    g = torch.Generator().manual_seed(1)
+    wq = torch.empty(work.H * work.d).uniform_(0.5, 1.5, generator=g).to(torch.bfloat16).to(dev)
+    wk = torch.empty(work.H * work.d).uniform_(0.5, 1.5, generator=g).to(torch.bfloat16).to(dev)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+
+    def step():
+        ea.qk_rmsnorm(q, k, wq, wk, 1e-6, q_out=qo, k_out=ko)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    alg_bytes = 2 * (q.numel() + k.numel()) * 2 + 2 * wq.numel() * 2   # Q, K read and written once; weights
+    ms_step = wall * 1e3 / steps
+    avg = float(np.mean(per))
+    result = {
+        "metric": "QK-RMSNorm across heads of Q and K (HBM GB/s)",
+        "value": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (the bf16 N(0,1) Q and K of the default workload, uniform weights)",
+        "config": {"workload": "qknorm_" + work.name, "shape": list(q.shape)},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (avg * 1e-3) / 1e9, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(alg_bytes / (avg * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "kernel": "qk_rmsnorm_kernel", "avg_launch_us": round(avg * 1e3, 2),
+                     "algorithmic_bytes_per_launch": alg_bytes},
+    }
+    if cpu:
+        from oracle import attn_oracle
+
+        orc = attn_oracle.get()
+        a = x.q[:1].double().numpy()            # one batch entry of Q (all heads, all tokens)
+        w64 = wq.cpu().double().numpy()
+        reps, t1 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t1 < 2.0:
+            orc.rmsnorm_across_heads(a, w64, 1e-6)
+            reps += 1
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(reps * a.size * 4 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"batch entry 0 of Q ({a.size} elements, bf16 bytes in and out), "
+                                            f"{reps} repetitions, single-threaded fp64; {dt:.2f} s"}
     print(json.dumps(result), flush=True)
     return 0
 

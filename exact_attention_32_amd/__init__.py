@@ -53,6 +53,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.attn_fwd_set_policy.argtypes = [ci, ci, ci, ci]
     L.attn_fwd_schedule.restype = ci
     L.attn_fwd_schedule.argtypes = [ci, ci, ci]
+    L.attn_qk_rmsnorm.restype = ci
+    L.attn_qk_rmsnorm.argtypes = [vp] * 6 + [ci] * 5 + [cf, ci, vp]
     if path == LIB_PATH:
         _lib = L
     return L
@@ -213,3 +215,32 @@ def quantize_e4m3(x: torch.Tensor, codes: torch.Tensor | None = None, descale: t
 def quantize_e5m2(x: torch.Tensor, codes: torch.Tensor | None = None, descale: torch.Tensor | None = None):
     """quantize_fp8 with fmt="e5m2"."""
     return quantize_fp8(x, "e5m2", codes, descale)
+
+
+def qk_rmsnorm(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, eps: float = 1e-6,
+               q_out: torch.Tensor | None = None, k_out: torch.Tensor | None = None, inplace: bool = False):
+    """RMSNorm of q [B, H, S_q, d] and k [B, H, S_k, d] across heads (one RMS per token over all
+    H*d channels), times the per-channel weights w_q, w_k [H*d]; bf16 or fp16 throughout.
+
+    Returns (q_norm, k_norm); with inplace=True they are q and k themselves.
+    """
+    B, H, S_q, S_k, d = _shapes(q, k, k)
+    for t in (q, k, w_q, w_k):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, w_q, w_k must be contiguous device tensors of one dtype")
+    if w_q.numel() != H * d or w_k.numel() != H * d:
+        raise ValueError("w_q and w_k must have H*d entries")
+    dt = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if inplace:
+        q_out, k_out = q, k
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    for t, ref in ((q_out, q), (k_out, k)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or t.device != ref.device:
+            raise ValueError("outputs must be contiguous tensors of the inputs' shape and dtype")
+    rc = load_library().attn_qk_rmsnorm(q.data_ptr(), k.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), q_out.data_ptr(),
+                                        k_out.data_ptr(), B, H, S_q, S_k, d, float(eps), dt, _stream(q.device))
+    _check(rc)
+    return q_out, k_out

@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
-SOURCES = [SRC, os.path.join(PKG, "csrc", "quantize.hip")]
+SOURCES = [SRC, os.path.join(PKG, "csrc", "quantize.hip"), os.path.join(PKG, "csrc", "qknorm.hip")]
 LIB = os.path.join(PKG, "libattn_fwd.so")
 
 HIPCC_FLAGS = [

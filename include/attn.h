@@ -122,6 +122,23 @@ int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *descale, in
 int attn_quantize_e5m2(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
                        void *stream);
 
+/*
+ * RMSNorm of Q and K across heads, the step before attention in the sglang
+ * QKNorm-across-heads write-up (blog.secrett2633): for every token, one RMS
+ * over its whole hidden vector (the H*d values of all heads), then
+ *   out[b,h,s,t] = x[b,h,s,t] * rsqrt(eps + sum_{h',t'} x[b,h',s,t']^2 / (H*d)) * w[h*d + t]
+ * computed in fp32 and stored rounded to nearest even in the tensor's type.
+ *   q, q_out  : device pointers, [B][H][S_q][d]; k, k_out: [B][H][S_k][d]
+ *   w_q, w_k  : device pointers, [H*d] per-channel weights
+ *   dtype     : ATTN_BF16 or ATTN_F16 for all six tensors
+ *   eps       : finite, >= 0;  d: 64 or 128;  H*d <= 8192
+ * In place is allowed (q_out == q and/or k_out == k); other overlaps are
+ * undefined.  All pointers 16-byte aligned.  The outputs are attn_fwd's q and
+ * k.  Returns an attn_status.
+ */
+int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, const void *w_k, void *q_out, void *k_out,
+                    int B, int H, int S_q, int S_k, int d, float eps, int dtype, void *stream);
+
 /* Schedules of the f16/bf16 kernel (attn_fwd_set_policy). */
 typedef enum {
     ATTN_SCHED_DEFAULT = 0,   /* the library's measured policy table */

@@ -33,7 +33,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e5m2", "attn_status_string", "attn_fwd_plan",
-                          "attn_quantize_e4m3", "attn_quantize_e5m2", "attn_fwd_set_policy"}
+                          "attn_quantize_e4m3", "attn_quantize_e5m2", "attn_fwd_set_policy", "attn_qk_rmsnorm"}
     for n in names:
         assert hasattr(lib, n), f"library does not export {n}"
 
@@ -159,3 +159,20 @@ def test_set_policy(lib):
     finally:
         assert lib.attn_fwd_set_policy(ea.ATTN_SCHED_DEFAULT, 0, 0, 0) == OK
     assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 64, 8)
+
+
+def callqn(lib, q=P, k=P, wq=P, wk=P, qo=P, ko=P, B=1, H=2, Sq=16, Sk=16, d=128, eps=1e-6, dtype=1):
+    return lib.attn_qk_rmsnorm(q, k, wq, wk, qo, ko, B, H, Sq, Sk, d, eps, dtype, None)
+
+
+def test_qk_rmsnorm_validation(lib):
+    for kw in ("q", "k", "wq", "wk", "qo", "ko"):
+        assert callqn(lib, **{kw: None}) == NULL
+        assert callqn(lib, **{kw: P + 8}) == ALIGN
+    for kw in ("B", "H", "Sq", "Sk"):
+        assert callqn(lib, **{kw: 0}) == SHAPE
+    assert callqn(lib, d=96) == UNSUP and callqn(lib, dtype=2) == UNSUP and callqn(lib, dtype=3) == UNSUP
+    assert callqn(lib, H=65, d=128) == UNSUP and callqn(lib, H=129, d=64) == UNSUP
+    for e in (-1e-6, float("nan"), float("inf")):
+        assert callqn(lib, eps=e) == VALUE
+    assert callqn(lib, B=2 ** 16, Sq=2 ** 16) == OVERFLOW
