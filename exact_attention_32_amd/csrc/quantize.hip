@@ -9,16 +9,21 @@
 //
 // The path is HBM-bound (4, 2 or 2 bytes in and 1 byte out per element), so the
 // kernel is one read of the block into registers, one reduction, one write:
-// a workgroup of 256 threads owns one 128-row block (128 x d elements), each
-// thread holds d/8 groups of 4 consecutive elements (coalesced 16- or 8-byte
-// loads, 4-byte code stores).
+// a workgroup of 4 d threads owns one 128-row block (128 x d elements), each
+// thread holds 8 groups of 4 consecutive elements (coalesced 16- or 8-byte
+// loads, 4-byte code stores); 32 data registers per thread leave room for 8
+// waves per SIMD, so many loads are in flight.
 //
 // Exact rounding: the fp32 quotient q = RN(x / descale) and the exact quotient
-// lie on the same side of every E4M3 midpoint unless q is itself a midpoint
+// lie on the same side of every code midpoint unless q is itself a midpoint
 // (a midpoint between them would be a closer float), so only then is the exact
 // residual x - q * descale (one FMA, exact for a correctly rounded quotient)
 // consulted, and q is moved one float towards the exact quotient before the
-// hardware's round-to-nearest-even conversion.
+// hardware's round-to-nearest-even conversion.  The correctly rounded division
+// is a long instruction sequence, so the common case takes x * RN(1 / descale)
+// instead: that product is within 2 floats of the exact quotient, so its code is
+// the exact quotient's unless a midpoint lies within 4 floats of it; only those
+// elements (and the subnormal range) take the exact path.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -33,7 +38,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int QBLK = 128;    // rows per scale block
-constexpr int QTHREADS = 256;
+constexpr int QPER = 8;      // groups of 4 elements per thread
+template <int D> constexpr int qthreads() { return QBLK * D / 4 / QPER; }   // 512 (d = 128), 256 (d = 64)
 
 template <class In> __device__ __forceinline__ f32x4 load4(const In *p);
 template <> __device__ __forceinline__ f32x4 load4<float>(const float *p) {
@@ -73,7 +79,7 @@ template <> struct Fp8Fmt<1> {   // E5M2: 2 mantissa bits, subnormal spacing 2^-
 
 // x / ds as the float that the hardware's nearest-even conversion maps to the code of the exact
 // quotient (see the file comment); |result| <= fmax
-template <int FMT> __device__ __forceinline__ float quotient(float x, float ds) {
+template <int FMT> __device__ __forceinline__ float quotient_exact(float x, float ds) {
     using F = Fp8Fmt<FMT>;
     float q = x / ds;   // correctly rounded division
     const float a = fabsf(q);
@@ -95,6 +101,18 @@ template <int FMT> __device__ __forceinline__ float quotient(float x, float ds) 
     return q;
 }
 
+// The same result, with inv = RN(1 / ds): the product when no code midpoint can lie between it
+// and the exact quotient, else quotient_exact
+template <int FMT> __device__ __forceinline__ float quotient(float x, float ds, float inv) {
+    using F = Fp8Fmt<FMT>;
+    const float q = x * inv;
+    const float a = fabsf(q);
+    if (a >= F::fmax) return copysignf(F::fmax, q);
+    bool near = true;   // subnormal range: always the exact path
+    if (a >= F::min_normal) near = (__float_as_uint(a) & F::low_mask) - (F::half - 4u) <= 8u;
+    return near ? quotient_exact<FMT>(x, ds) : q;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -113,9 +131,9 @@ template <> __device__ __forceinline__ uint32_t pack4<1>(float a, float b, float
 }
 
 template <int D, class In, int FMT>
-__global__ __launch_bounds__(QTHREADS) void quantize_fp8_kernel(const In *__restrict__ x, uint32_t *__restrict__ codes,
-                                                                float *__restrict__ descale, int S, int nblk) {
-    constexpr int PER = QBLK * D / 4 / QTHREADS;   // groups of 4 elements per thread
+__global__ __launch_bounds__(qthreads<D>()) void quantize_fp8_kernel(const In *__restrict__ x, uint32_t *__restrict__ codes,
+                                                                    float *__restrict__ descale, int S, int nblk) {
+    constexpr int QTHREADS = qthreads<D>(), PER = QPER;
     static_assert(PER * 4 * QTHREADS == QBLK * D, "block shape");
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;
@@ -140,15 +158,18 @@ __global__ __launch_bounds__(QTHREADS) void quantize_fp8_kernel(const In *__rest
     amax = wave_max(amax);
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    amax = red[0];
+#pragma unroll
+    for (int i = 1; i < QTHREADS / 64; ++i) amax = fmaxf(amax, red[i]);
     const float ds = amax > 0.0f ? amax / Fp8Fmt<FMT>::fmax : 1.0f;
+    const float inv = 1.0f / ds;
     if (tid == 0) descale[blk] = ds;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
         const int g = tid + p * QTHREADS;
         if ((4 * g) / D < rows) {
-            codes[(base + 4 * g) / 4] = pack4<FMT>(quotient<FMT>(v[p][0], ds), quotient<FMT>(v[p][1], ds),
-                                                   quotient<FMT>(v[p][2], ds), quotient<FMT>(v[p][3], ds));
+            codes[(base + 4 * g) / 4] = pack4<FMT>(quotient<FMT>(v[p][0], ds, inv), quotient<FMT>(v[p][1], ds, inv),
+                                                   quotient<FMT>(v[p][2], ds, inv), quotient<FMT>(v[p][3], ds, inv));
         }
     }
 }
@@ -156,6 +177,7 @@ __global__ __launch_bounds__(QTHREADS) void quantize_fp8_kernel(const In *__rest
 template <int D, int FMT>
 int launch_quant(const void *x, int dtype, void *codes, float *descale, int nwg, int S, int nblk, hipStream_t s) {
     uint32_t *c = static_cast<uint32_t *>(codes);
+    constexpr int QTHREADS = qthreads<D>();
     if (dtype == ATTN_F32)
         hipLaunchKernelGGL((quantize_fp8_kernel<D, float, FMT>), dim3(nwg), dim3(QTHREADS), 0, s,
                            static_cast<const float *>(x), c, descale, S, nblk);
