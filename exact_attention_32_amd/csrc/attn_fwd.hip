@@ -1088,9 +1088,11 @@ __device__ __forceinline__ f32x16 mfma_f8(const i32x8 &a, const i32x8 &b, const 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
 }
 
-// four floats -> four E4M3 bytes (round to nearest even), first value in the low byte
+// four floats -> four E4M3 bytes (round to nearest even), first value in the low byte.  The
+// first conversion's "old" operand only supplies bytes 2-3, which the second one overwrites, so
+// any register does (a's bits: no zero has to be materialised).
 __device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -1189,19 +1191,19 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
 
     auto compute = [&](int t, uint32_t kt, uint32_t vt, bool masked) __attribute__((always_inline)) {
         const int k0 = t * BC;
-        // the per-lane offsets pass through an empty asm here, so that the compiler forms each
-        // fetch address as lane offset + stage base + immediate inside the tile instead of keeping
-        // every (offset + immediate) sum live in its own register across the loop
-        int ko[2 * KSTEPS], vo[D / 32];
+        // one address per lane offset and tile (stage base + lane offset), passed through an empty
+        // asm so that the compiler neither keeps every (offset + immediate) sum live across the loop
+        // nor re-derives the stage base per fetch: each fetch is that address + an immediate
+        uint32_t ka[2 * KSTEPS], va[D / 32];
 #pragma unroll
         for (int j = 0; j < 2 * KSTEPS; ++j) {
-            ko[j] = koff[j];
-            asm volatile("" : "+v"(ko[j]));
+            ka[j] = kt + (uint32_t)koff[j];
+            asm volatile("" : "+v"(ka[j]));
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            vo[db] = vlane[db];
-            asm volatile("" : "+v"(vo[db]));
+            va[db] = vt + (uint32_t)vlane[db];
+            asm volatile("" : "+v"(va[db]));
         }
         // descales through the constant address space: wave-uniform scalar loads, which the
         // vector-memory counter that paces the K/V pipeline does not see
@@ -1218,8 +1220,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             constexpr int ks = decltype(KS)::value;
             static_for<BC / 32>([&](auto KB) {
                 constexpr int kb2 = decltype(KB)::value;
-                const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(kt + ko[2 * ks]);
-                const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(kt + ko[2 * ks + 1]);
+                const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks]);
+                const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks + 1]);
                 const i32x8 a = __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
                 s[kb2] = mfma_f8<FMT, FMT>(a, qf[ks], s[kb2]);
             });
@@ -1288,11 +1290,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
         constexpr int NPV = (BC / 64) * (D / 32), PV_AHEAD = 2;
         auto pv_fetch = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value, kk = i / (D / 32), db = i % (D / 32);
-            const uint32_t va = vt + vo[db];
-            const u32x2 r0 = lds_load_tr8<(64 * kk + 0) * ROWB>(va);
-            const u32x2 r1 = lds_load_tr8<(64 * kk + 16) * ROWB>(va);
-            const u32x2 r2 = lds_load_tr8<(64 * kk + 32) * ROWB>(va);
-            const u32x2 r3 = lds_load_tr8<(64 * kk + 48) * ROWB>(va);
+            const u32x2 r0 = lds_load_tr8<(64 * kk + 0) * ROWB>(va[db]);
+            const u32x2 r1 = lds_load_tr8<(64 * kk + 16) * ROWB>(va[db]);
+            const u32x2 r2 = lds_load_tr8<(64 * kk + 32) * ROWB>(va[db]);
+            const u32x2 r3 = lds_load_tr8<(64 * kk + 48) * ROWB>(va[db]);
             return __builtin_bit_cast(i32x8, (u32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]});
         };
         i32x8 ring[PV_AHEAD];
