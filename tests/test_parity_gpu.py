@@ -175,3 +175,24 @@ def test_workload_sampled_rows(oracle, name):
     assert st["pass"], st
     # properties at every row: finite outputs; LSE of a causal row i is >= log-free bound: LSE >= s_ii
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("name", ["fp8_b2_h16_s4096_d128", "e5m2_b2_h16_s4096_d128"])
+def test_fp8_quantisation_error_report(oracle, name):
+    """Reported, not gated: the fp8 path against attention on the unquantised fp32 draws (the
+    error that block quantisation itself adds), on sampled rows of the full-size workload."""
+    w = I.WORKLOADS[name]
+    x = I.make_inputs(w)
+    U.say(f"[gpu] quantisation error report {name}")
+    o, lse = U.run_gpu(x)
+    o = o.view(w.B * w.H, w.S_q, w.d)
+    lse = lse.view(w.B * w.H, w.S_q)
+    rows = U.sample_rows(w, n_random=100, seed=w.seed + 100)
+    og = o[rows[:, 0], rows[:, 1]].double().cpu().numpy()
+    lg = lse[rows[:, 0], rows[:, 1]].double().cpu().numpy()
+    ro, rl = oracle.attention_rows(x.q32.astype(np.float64), x.k32.astype(np.float64), x.v32.astype(np.float64),
+                                   w.causal, w.scale, rows)
+    err_o, err_l = np.abs(og - ro), np.abs(lg - rl)
+    U.say(f"   vs unquantised fp32 inputs: max|dO| {err_o.max():.3e} rms {np.sqrt((err_o ** 2).mean()):.3e}, "
+          f"max|dLSE| {err_l.max():.3e}")
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
