@@ -87,15 +87,9 @@ template <> __device__ __forceinline__ float sum2<F16>(uint32_t a, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), one, acc, false);
 }
 
-#ifndef ATTN_LAZY
-#define ATTN_LAZY 1
-#endif
-#ifndef ATTN_PRIO
-#define ATTN_PRIO 0
-#endif
 // The running max moves only when a row's max would grow by more than RESCALE_LOG2 (base 2);
 // until then p = exp2(s*c - m) <= 2^RESCALE_LOG2 and the O rescale is skipped.
-constexpr float RESCALE_LOG2 = ATTN_LAZY ? 8.0f : 0.0f;
+constexpr float RESCALE_LOG2 = 8.0f;
 
 // Row max between lane l and lane l^32 (the two halves of a 32x32 accumulator column).
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -157,20 +151,6 @@ template <int I, int N, class F> __device__ __forceinline__ void static_for_impl
     }
 }
 template <int N, class F> __device__ __forceinline__ void static_for(F &&f) { static_for_impl<0, N>(f); }
-
-// Instruction-scheduling hint for a block of NSTEP k-steps, each READS_PER LDS reads feeding
-// MFMA_PER MFMAs: PRE reads first, then alternately the MFMAs of one step and the reads of a
-// later one, so that LDS latency overlaps the matrix core instead of stalling every MFMA.
-template <int PRE, int READS_PER, int MFMA_PER, int NSTEP>
-__device__ __forceinline__ void sched_reads_ahead() {
-    constexpr int DS_READ = 0x100, MFMA = 0x008;
-    __builtin_amdgcn_sched_group_barrier(DS_READ, PRE, 0);
-#pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-        __builtin_amdgcn_sched_group_barrier(MFMA, MFMA_PER, 0);
-        __builtin_amdgcn_sched_group_barrier(DS_READ, READS_PER, 0);
-    }
-}
 
 // ds_read_b64_tr_b16: inside each group of 16 lanes, lane j receives element (j % 4) of the
 // 8-byte words addressed by lanes 4k + j/4, for k = 0..3.
@@ -330,7 +310,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                        __attribute__((always_inline)) {
         const int k0 = t * BC;
         // S^T = K Q^T
-        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
         f32x16 s[QB][BC / 32];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -347,7 +326,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                 for (int qb = 0; qb < QB; ++qb) s[qb][kb2] = mfma_32x32x16<T>(a, qf[qb][ks], s[qb][kb2]);
             }
         }
-        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
         if (masked) {
             // element i of block kb2 holds key k0 + 4g + c with c = 32 kb2 + 8 (i / 4) + i % 4 (a
             // constant); it is visible iff c < lim
@@ -411,12 +389,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                                            pack2<T>(s[qb][kb2][o + 4], s[qb][kb2][o + 5]),
                                            pack2<T>(s[qb][kb2][o + 6], s[qb][kb2][o + 7])};
                     pf[qb][kb2 * 2 + h] = pk;
-                    if (ATTN_LAZY) lr = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr))));
+                    lr = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr))));
                 }
             lrnd[qb] = lr;
         }
         // O^T += V^T P^T; V^T is fetched with two transposing LDS reads per operand
-        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < BC / 16; ++ks) {
 #pragma unroll
@@ -428,7 +405,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                 for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_32x32x16<T>(a, pf[qb][ks], oacc[qb][db]);
             }
         }
-        if (ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
     };
 
     constexpr int LPT = 2 * BPW;   // direct-to-LDS loads per tile per wave
@@ -476,7 +452,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float lt = xhalf_sum(lrow[qb]);
-        const float inv = 1.0f / (ATTN_LAZY ? xhalf_sum(lrnd[qb]) : lt);
+        const float inv = 1.0f / xhalf_sum(lrnd[qb]);
         const int qrow = qw0 + qb * 32 + l32;
         if (qrow < Sq) {
             uint16_t *orow = p.o + ((size_t)bh * Sq + qrow) * D;
@@ -987,7 +963,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
                 const u32x4 pk = u32x4{pack2<T>(s[kb2][o + 0], s[kb2][o + 1]), pack2<T>(s[kb2][o + 2], s[kb2][o + 3]),
                                        pack2<T>(s[kb2][o + 4], s[kb2][o + 5]), pack2<T>(s[kb2][o + 6], s[kb2][o + 7])};
                 pf[kb2 * 2 + h] = pk;
-                if (ATTN_LAZY) lr[h] = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr[h]))));
+                lr[h] = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr[h]))));
             }
         lrow += (ls[0] + ls[1]) + (ls[2] + ls[3]);
         lrnd += lr[0] + lr[1];
@@ -1025,7 +1001,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
 
     // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
     const float lt = xhalf_sum(lrow);
-    const float inv = 1.0f / (ATTN_LAZY ? xhalf_sum(lrnd) : lt);
+    const float inv = 1.0f / xhalf_sum(lrnd);
     const int qrow = qw0 + l32;
     if (qrow < Sq) {
         uint16_t *orow = p.o + ((size_t)bh * Sq + qrow) * D;
