@@ -1366,7 +1366,10 @@ int check_common(const void *q, const void *k, const void *v, const void *o, con
 constexpr int kShapes[][4] = {{ATTN_SCHED_CLASSIC, 1, 8, 3},  {ATTN_SCHED_CLASSIC, 1, 8, 4},
                               {ATTN_SCHED_CLASSIC, 2, 4, 3},  {ATTN_SCHED_CLASSIC, 2, 4, 4},
                               {ATTN_SCHED_CLASSIC, 1, 4, 2},  {ATTN_SCHED_CLASSIC, 1, 4, 3},
-                              {ATTN_SCHED_PINGPONG, 1, 8, 3}, {ATTN_SCHED_DEPHASED, 1, 8, 4}};
+                              {ATTN_SCHED_PINGPONG, 1, 8, 3}, {ATTN_SCHED_DEPHASED, 1, 8, 4},
+                              {ATTN_SCHED_CLASSIC, 2, 8, 3},  {ATTN_SCHED_CLASSIC, 2, 8, 4}};
+// (2, 8, *) holds 64 queries per wave at two waves per SIMD, which fits the registers at d = 64
+// only; at d = 128 a launch with it returns ATTN_ERR_UNSUPPORTED.
 
 bool compiled_shape(int sched, int qb, int nw, int ns) {
     for (const auto &sh : kShapes)
@@ -1391,15 +1394,18 @@ int policy_override() {
     return g_override.load(std::memory_order_relaxed);
 }
 
-// Tile policy per head dimension, measured on MI355X (bf16, B=2 H=16 S=4096, B=4 H=16 S=2048 and
-// causal B=1 H=32 S=8192 at d=128; causal B=1 H=16 S=16384 at d=64): the de-phased schedule is
-// 1.5-2% faster than the classic one at d=128 and 3% slower at d=64.
-void choose_policy(int d, int causal, Plan *pl) {
+// Tile policy, measured on MI355X (bf16, B=2 H=16 S=4096, B=4 H=16 S=2048 and causal B=1 H=32
+// S=8192 at d=128; causal B=1 H=16 S=16384 and B=1 H=2 S=128 at d=64): at d=128 the de-phased
+// schedule is 1.5-2% faster than the classic one; at d=64 it is 3% slower, and the classic
+// schedule with 64 queries per wave (2, 8, 4) is 7% faster than with 32 (1, 8, 4) as long as its
+// 512-query workgroups fill the 256 CUs (slower on the tiny S=128 workload, which they do not).
+void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
     (void)causal;
     pl->sched = d == 128 ? ATTN_SCHED_DEPHASED : ATTN_SCHED_CLASSIC;
     pl->qb = 1;
     pl->nw = 8;
     pl->ns = 4;
+    if (d == 64 && (long long)B * H * ((Sq + 511) / 512) >= 256) pl->qb = 2;
     const int ov = policy_override();
     if (ov > 0) {
         pl->sched = ov & 255;
@@ -1410,7 +1416,8 @@ void choose_policy(int d, int causal, Plan *pl) {
 }
 
 int make_plan(int B, int H, int Sq, int d, int causal, Plan *pl) {
-    choose_policy(d, causal, pl);
+    choose_policy(B, H, Sq, d, causal, pl);
+    if (pl->qb == 2 && pl->nw == 8 && d != 64) return ATTN_ERR_UNSUPPORTED;   // registers: d = 64 only
     pl->block_q = pl->nw * pl->qb * 32;
     pl->block_k = 64;
     pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
@@ -1444,6 +1451,12 @@ int launch_shape(const Params &p, const Plan &pl, hipStream_t s) {
         case 244: return launch<T, D, CAUSAL, 2, 4, 4>(p, pl, s);
         case 142: return launch<T, D, CAUSAL, 1, 4, 2>(p, pl, s);
         case 143: return launch<T, D, CAUSAL, 1, 4, 3>(p, pl, s);
+        case 283:
+            if constexpr (D == 64) return launch<T, D, CAUSAL, 2, 8, 3>(p, pl, s);
+            return ATTN_ERR_UNSUPPORTED;
+        case 284:
+            if constexpr (D == 64) return launch<T, D, CAUSAL, 2, 8, 4>(p, pl, s);
+            return ATTN_ERR_UNSUPPORTED;
         default: return ATTN_ERR_UNSUPPORTED;
     }
 }
@@ -1594,7 +1607,7 @@ extern "C" int attn_fwd_schedule(int d, int causal, int dtype) {
     if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2) return ATTN_SCHED_DEFAULT;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return -ATTN_ERR_UNSUPPORTED;
     Plan pl;
-    choose_policy(d, causal, &pl);
+    choose_policy(1, 1, 1, d, causal, &pl);
     return pl.sched;
 }
 

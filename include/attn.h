@@ -152,7 +152,9 @@ typedef enum {
  * process use one compiled schedule and tile shape (qb 32-query blocks per
  * wave, nw waves per workgroup, ns LDS stages) instead of the measured policy
  * table.  Compiled: CLASSIC (1,8,3) (1,8,4) (2,4,3) (2,4,4) (1,4,2) (1,4,3),
- * PINGPONG (1,8,3), DEPHASED (1,8,4).  schedule = ATTN_SCHED_DEFAULT restores
+ * and for d = 64 only (2,8,3) (2,8,4) (attn_fwd then returns
+ * ATTN_ERR_UNSUPPORTED at d = 128); PINGPONG (1,8,3); DEPHASED (1,8,4).
+ * schedule = ATTN_SCHED_DEFAULT restores
  * the table (the other arguments are then ignored).  The environment variable
  * ATTN_FWD_POLICY="schedule,qb,nw,ns", read at the first call, sets the same
  * override.  Process-wide, not tied to a stream: calls in flight keep the

@@ -143,6 +143,7 @@ def test_quantize_validation(lib):
 COMPILED = [(ea.ATTN_SCHED_CLASSIC, 1, 8, 3), (ea.ATTN_SCHED_CLASSIC, 1, 8, 4), (ea.ATTN_SCHED_CLASSIC, 2, 4, 3),
             (ea.ATTN_SCHED_CLASSIC, 2, 4, 4), (ea.ATTN_SCHED_CLASSIC, 1, 4, 2), (ea.ATTN_SCHED_CLASSIC, 1, 4, 3),
             (ea.ATTN_SCHED_PINGPONG, 1, 8, 3), (ea.ATTN_SCHED_DEPHASED, 1, 8, 4)]
+D64_ONLY = [(ea.ATTN_SCHED_CLASSIC, 2, 8, 3), (ea.ATTN_SCHED_CLASSIC, 2, 8, 4)]
 
 
 def test_set_policy(lib):
@@ -156,9 +157,17 @@ def test_set_policy(lib):
             assert (bq, bk, w) == (qb * nw * 32, 64, nw) and n == -(-4096 // bq) * 32
             # fp8 plans do not follow the f16/bf16 override
             assert ea.plan(2, 16, 4096, 4096, 128, False, dtype=ea.ATTN_FP8_E4M3)[:3] == (256, 128, 8)
+        for sched, qb, nw, ns in D64_ONLY:
+            assert lib.attn_fwd_set_policy(sched, qb, nw, ns) == OK
+            assert ea.plan(1, 16, 4096, 4096, 64, False)[:3] == (512, 64, 8)
+            with pytest.raises(ea.AttnError):
+                ea.plan(1, 16, 4096, 4096, 128, False)
     finally:
         assert lib.attn_fwd_set_policy(ea.ATTN_SCHED_DEFAULT, 0, 0, 0) == OK
     assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 64, 8)
+    # d = 64: 64 queries per wave once the 512-query workgroups fill the 256 CUs
+    assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (512, 64, 8)
+    assert ea.plan(1, 2, 128, 128, 64, False)[:3] == (256, 64, 8)
 
 
 def callqn(lib, q=P, k=P, wq=P, wk=P, qo=P, ko=P, B=1, H=2, Sq=16, Sk=16, d=128, eps=1e-6, dtype=1):
