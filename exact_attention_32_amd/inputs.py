@@ -223,3 +223,28 @@ def random_workload(B: int, H: int, S_q: int, S_k: int, d: int, dtype: str, caus
                     outliers: bool = False) -> Workload:
     return Workload(f"{dtype}{'_causal' if causal else ''}_b{B}_h{H}_sq{S_q}_sk{S_k}_d{d}", B, H, S_q, S_k, d,
                     dtype, causal, seed, outliers)
+
+
+def make_device_inputs(B: int, H: int, S: int, d: int, dtype: str, seed: int, device="cuda:0"):
+    """Seeded inputs generated directly in device memory, for sizes whose host-side draw would be
+    slow (beyond 2^31 elements per tensor): torch's generator on the device, ``randn`` in fp32
+    in the order Q, K, V, then the RNE cast to bf16/f16.  For "fp8"/"e5m2" the tensors are
+    uniformly random finite codes of that format (no NaN or infinity codes) with per-(b, h,
+    128-row block) descales uniform in [0.5, 2): synthetic quantised data, not a quantisation
+    of anything.  The codes are those of magnitude below 2 (0x00-0x3f and 0x80-0xbf in both
+    formats, subnormals included), so that scores stay in the range of N(0, 1) data.
+    Returns (q, k, v, descales or None); descales are (q_ds, k_ds, v_ds)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    shape = (B, H, S, d)
+    if not is_fp8(dtype):
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        out = [torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(tdt) for _ in range(3)]
+        return out[0], out[1], out[2], None
+    out = []
+    for _ in range(3):
+        mag = torch.randint(0, 0x40, shape, generator=g, device=device, dtype=torch.int32)
+        sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32) * 0x80
+        out.append((mag + sign).to(torch.uint8))
+    ds = tuple(torch.rand((B, H, _nblk(S)), generator=g, device=device, dtype=torch.float32) * 1.5 + 0.5
+               for _ in range(3))
+    return out[0], out[1], out[2], ds
