@@ -53,6 +53,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.attn_fwd_set_policy.argtypes = [ci, ci, ci, ci]
     L.attn_fwd_schedule.restype = ci
     L.attn_fwd_schedule.argtypes = [ci, ci, ci]
+    L.attn_quantize_qkv.restype = ci
+    L.attn_quantize_qkv.argtypes = [vp, vp, vp, ci, ci] + [vp] * 6 + [ci] * 5 + [vp]
     L.attn_qk_rmsnorm.restype = ci
     L.attn_qk_rmsnorm.argtypes = [vp] * 6 + [ci] * 5 + [cf, ci, vp]
     if path == LIB_PATH:
@@ -205,6 +207,31 @@ def quantize_fp8(x: torch.Tensor, fmt: str = "e4m3", codes: torch.Tensor | None 
     rc = entry(x.data_ptr(), dt, codes.data_ptr(), descale.data_ptr(), B, H, S, d, _stream(x.device))
     _check(rc)
     return codes, descale
+
+
+def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fmt: str = "e4m3"):
+    """Per-block fp8 quantisation of q [B, H, S_q, d], k and v [B, H, S_k, d] in one launch.
+
+    Returns ((q_codes, k_codes, v_codes), (q_descale, k_descale, v_descale)), bit-identical to three
+    quantize_fp8 calls: the inputs of fwd_fp8 with the same fmt.
+    """
+    if fmt not in _FP8_TORCH:
+        raise ValueError(f"fmt must be 'e4m3' or 'e5m2', not {fmt!r}")
+    B, H, S_q, S_k, d = _shapes(q, k, v)
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    dt = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    codes = tuple(torch.empty(t.shape, dtype=torch.uint8, device=t.device) for t in (q, k, v))
+    descales = tuple(torch.empty((B, H, (s + 127) // 128), dtype=torch.float32, device=q.device)
+                     for s in (S_q, S_k, S_k))
+    rc = load_library().attn_quantize_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dt,
+                                          ATTN_FP8_E4M3 if fmt == "e4m3" else ATTN_FP8_E5M2,
+                                          *[c.data_ptr() for c in codes], *[x.data_ptr() for x in descales],
+                                          B, H, S_q, S_k, d, _stream(q.device))
+    _check(rc)
+    return codes, descales
 
 
 def quantize_e4m3(x: torch.Tensor, codes: torch.Tensor | None = None, descale: torch.Tensor | None = None):

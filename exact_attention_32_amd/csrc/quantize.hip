@@ -130,13 +130,27 @@ template <> __device__ __forceinline__ uint32_t pack4<1>(float a, float b, float
     return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
 }
 
+// Up to three tensors (Q, K, V) per launch: blockIdx.y selects the tensor, blockIdx.x the
+// (b, h, 128-row block).
+struct QuantParams {
+    const void *x[3];
+    uint32_t *codes[3];
+    float *descale[3];
+    int S[3], nblk[3], nwg[3];
+};
+
 template <int D, class In, int FMT>
-__global__ __launch_bounds__(qthreads<D>()) void quantize_fp8_kernel(const In *__restrict__ x, uint32_t *__restrict__ codes,
-                                                                    float *__restrict__ descale, int S, int nblk) {
+__global__ __launch_bounds__(qthreads<D>()) void quantize_fp8_kernel(QuantParams qp) {
     constexpr int QTHREADS = qthreads<D>(), PER = QPER;
     static_assert(PER * 4 * QTHREADS == QBLK * D, "block shape");
-    const int tid = threadIdx.x;
+    const int which = blockIdx.y;
     const int blk = blockIdx.x;
+    if (blk >= qp.nwg[which]) return;   // the whole workgroup leaves before its barrier
+    const In *__restrict__ x = static_cast<const In *>(qp.x[which]);
+    uint32_t *__restrict__ codes = qp.codes[which];
+    float *__restrict__ descale = qp.descale[which];
+    const int S = qp.S[which], nblk = qp.nblk[which];
+    const int tid = threadIdx.x;
     const int bh = blk / nblk, j = blk - bh * nblk;
     const int r0 = j * QBLK;
     const int rows = min(QBLK, S - r0);
@@ -175,36 +189,54 @@ __global__ __launch_bounds__(qthreads<D>()) void quantize_fp8_kernel(const In *_
 }
 
 template <int D, int FMT>
-int launch_quant(const void *x, int dtype, void *codes, float *descale, int nwg, int S, int nblk, hipStream_t s) {
-    uint32_t *c = static_cast<uint32_t *>(codes);
+int launch_quant(const QuantParams &qp, int ntensors, int dtype, hipStream_t s) {
     constexpr int QTHREADS = qthreads<D>();
+    int gx = 0;
+    for (int i = 0; i < ntensors; ++i) gx = qp.nwg[i] > gx ? qp.nwg[i] : gx;
+    const dim3 grid(gx, ntensors);
     if (dtype == ATTN_F32)
-        hipLaunchKernelGGL((quantize_fp8_kernel<D, float, FMT>), dim3(nwg), dim3(QTHREADS), 0, s,
-                           static_cast<const float *>(x), c, descale, S, nblk);
+        hipLaunchKernelGGL((quantize_fp8_kernel<D, float, FMT>), grid, dim3(QTHREADS), 0, s, qp);
     else if (dtype == ATTN_BF16)
-        hipLaunchKernelGGL((quantize_fp8_kernel<D, bf16_t, FMT>), dim3(nwg), dim3(QTHREADS), 0, s,
-                           static_cast<const bf16_t *>(x), c, descale, S, nblk);
+        hipLaunchKernelGGL((quantize_fp8_kernel<D, bf16_t, FMT>), grid, dim3(QTHREADS), 0, s, qp);
     else
-        hipLaunchKernelGGL((quantize_fp8_kernel<D, f16_t, FMT>), dim3(nwg), dim3(QTHREADS), 0, s,
-                           static_cast<const f16_t *>(x), c, descale, S, nblk);
+        hipLaunchKernelGGL((quantize_fp8_kernel<D, f16_t, FMT>), grid, dim3(QTHREADS), 0, s, qp);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-template <int FMT>
-int quantize(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d, void *stream) {
+// argument checks of one tensor; fills slot i of qp
+int check_tensor(const void *x, void *codes, float *descale, int B, int H, int S, QuantParams *qp, int i) {
     if (!x || !codes) return ATTN_ERR_NULL;
     if (!descale) return ATTN_ERR_DESCALE;
     if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
-    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15u) return ATTN_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(descale) & 3u) return ATTN_ERR_DESCALE;
     const long long nblk = (S + QBLK - 1) / QBLK;
     const long long nwg = (long long)B * H * nblk;
     if (nwg > INT_MAX || (long long)B * H > INT_MAX / S) return ATTN_ERR_OVERFLOW;
+    qp->x[i] = x;
+    qp->codes[i] = static_cast<uint32_t *>(codes);
+    qp->descale[i] = descale;
+    qp->S[i] = S;
+    qp->nblk[i] = (int)nblk;
+    qp->nwg[i] = (int)nwg;
+    return ATTN_OK;
+}
+
+int launch_checked(const QuantParams &qp, int ntensors, int dtype, int d, int fmt, void *stream) {
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (d == 128) return launch_quant<128, FMT>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
-    return launch_quant<64, FMT>(x, dtype, codes, descale, (int)nwg, S, (int)nblk, s);
+    if (fmt == 0)
+        return d == 128 ? launch_quant<128, 0>(qp, ntensors, dtype, s) : launch_quant<64, 0>(qp, ntensors, dtype, s);
+    return d == 128 ? launch_quant<128, 1>(qp, ntensors, dtype, s) : launch_quant<64, 1>(qp, ntensors, dtype, s);
+}
+
+template <int FMT>
+int quantize(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d, void *stream) {
+    QuantParams qp = {};
+    const int st = check_tensor(x, codes, descale, B, H, S, &qp, 0);
+    if (st != ATTN_OK) return st;
+    return launch_checked(qp, 1, dtype, d, FMT, stream);
 }
 
 }  // namespace
@@ -217,4 +249,16 @@ extern "C" int attn_quantize_e4m3(const void *x, int dtype, void *codes, float *
 extern "C" int attn_quantize_e5m2(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d,
                                   void *stream) {
     return quantize<1>(x, dtype, codes, descale, B, H, S, d, stream);
+}
+
+extern "C" int attn_quantize_qkv(const void *q, const void *k, const void *v, int dtype, int fmt, void *q_codes,
+                                 void *k_codes, void *v_codes, float *q_descale, float *k_descale, float *v_descale,
+                                 int B, int H, int S_q, int S_k, int d, void *stream) {
+    if (fmt != ATTN_FP8_E4M3 && fmt != ATTN_FP8_E5M2) return ATTN_ERR_UNSUPPORTED;
+    QuantParams qp = {};
+    int st = check_tensor(q, q_codes, q_descale, B, H, S_q, &qp, 0);
+    if (st == ATTN_OK) st = check_tensor(k, k_codes, k_descale, B, H, S_k, &qp, 1);
+    if (st == ATTN_OK) st = check_tensor(v, v_codes, v_descale, B, H, S_k, &qp, 2);
+    if (st != ATTN_OK) return st;
+    return launch_checked(qp, 3, dtype, d, fmt == ATTN_FP8_E5M2 ? 1 : 0, stream);
 }

@@ -123,6 +123,19 @@ int attn_quantize_e5m2(const void *x, int dtype, void *codes, float *descale, in
                        void *stream);
 
 /*
+ * The block quantisation of attn_quantize_e4m3 / attn_quantize_e5m2 for Q, K
+ * and V in one launch (the three inputs of attn_fwd_fp8 / attn_fwd_fp8_e5m2).
+ *   fmt      : ATTN_FP8_E4M3 or ATTN_FP8_E5M2
+ *   q        : [B][H][S_q][d], k and v: [B][H][S_k][d], all of type dtype
+ *   *_codes  : uint8, the inputs' shapes; *_descale: fp32 [B][H][ceil(S/128)]
+ * Results are bit-identical to the three single-tensor calls.  Argument
+ * checks, errors and ownership as for attn_quantize_e4m3.
+ */
+int attn_quantize_qkv(const void *q, const void *k, const void *v, int dtype, int fmt, void *q_codes, void *k_codes,
+                      void *v_codes, float *q_descale, float *k_descale, float *v_descale, int B, int H, int S_q,
+                      int S_k, int d, void *stream);
+
+/*
  * RMSNorm of Q and K across heads, the step before attention in the sglang
  * QKNorm-across-heads write-up (blog.secrett2633): for every token, one RMS
  * over its whole hidden vector (the H*d values of all heads), then

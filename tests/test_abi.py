@@ -33,7 +33,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e5m2", "attn_status_string", "attn_fwd_plan",
-                          "attn_quantize_e4m3", "attn_quantize_e5m2", "attn_fwd_set_policy", "attn_qk_rmsnorm"}
+                          "attn_quantize_e4m3", "attn_quantize_e5m2", "attn_fwd_set_policy", "attn_qk_rmsnorm",
+                          "attn_quantize_qkv"}
     for n in names:
         assert hasattr(lib, n), f"library does not export {n}"
 
@@ -185,3 +186,21 @@ def test_qk_rmsnorm_validation(lib):
     for e in (-1e-6, float("nan"), float("inf")):
         assert callqn(lib, eps=e) == VALUE
     assert callqn(lib, B=2 ** 16, Sq=2 ** 16) == OVERFLOW
+
+
+def callqkv(lib, q=P, k=P, v=P, dtype=3, fmt=2, cq=P, ck=P, cv=P, dq=P, dk=P, dv=P, B=1, H=1, Sq=16, Sk=16, d=128):
+    return lib.attn_quantize_qkv(q, k, v, dtype, fmt, cq, ck, cv, dq, dk, dv, B, H, Sq, Sk, d, None)
+
+
+def test_quantize_qkv_validation(lib):
+    for kw in ("q", "k", "v", "cq", "ck", "cv"):
+        assert callqkv(lib, **{kw: None}) == NULL
+    for kw in ("dq", "dk", "dv"):
+        assert callqkv(lib, **{kw: None}) == DESCALE and callqkv(lib, **{kw: P + 2}) == DESCALE
+    for kw in ("q", "k", "v", "cq", "ck", "cv"):
+        assert callqkv(lib, **{kw: P + 4}) == ALIGN
+    for kw in ("B", "H", "Sq", "Sk"):
+        assert callqkv(lib, **{kw: 0}) == SHAPE
+    assert callqkv(lib, fmt=0) == UNSUP and callqkv(lib, fmt=1) == UNSUP and callqkv(lib, fmt=3) == UNSUP
+    assert callqkv(lib, d=96) == UNSUP and callqkv(lib, dtype=2) == UNSUP
+    assert callqkv(lib, B=2 ** 16, H=2 ** 16, Sk=2 ** 10) == OVERFLOW

@@ -100,3 +100,20 @@ def test_quantized_inputs_drive_fp8_attention(oracle, fmt):
                         fmt=fmt)
     o2, l2 = U.run_gpu(x)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_quantize_qkv_equals_single_calls(oracle, fmt, dtype):
+    """One launch for Q, K, V (S_q != S_k) gives the bytes of three single-tensor calls."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    U.say(f"[gpu] quantize_qkv {fmt} {dtype}")
+    q = torch.from_numpy(_draw((2, 3, 300, 128), 11)).to(dtype).to(dev)
+    k = torch.from_numpy(_draw((2, 3, 513, 128), 12)).to(dtype).to(dev)
+    v = torch.from_numpy(_draw((2, 3, 513, 128), 13)).to(dtype).to(dev)
+    codes, ds = ea.quantize_qkv(q, k, v, fmt)
+    for t, c, d in zip((q, k, v), codes, ds):
+        c1, d1 = ea.quantize_fp8(t, fmt)
+        assert torch.equal(c, c1) and torch.equal(d, d1)
