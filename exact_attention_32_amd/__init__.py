@@ -50,7 +50,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.attn_quantize_e5m2.restype = ci
     L.attn_quantize_e5m2.argtypes = L.attn_quantize_e4m3.argtypes
     L.attn_fwd_set_policy.restype = ci
-    L.attn_fwd_set_policy.argtypes = [ci, ci, ci, ci]
+    L.attn_fwd_set_policy.argtypes = [ci, ci, ci, ci, ci]
     L.attn_fwd_schedule.restype = ci
     L.attn_fwd_schedule.argtypes = [ci, ci, ci]
     L.attn_quantize_qkv.restype = ci
@@ -78,10 +78,11 @@ def plan(B, H, S_q, S_k, d, causal=False, dtype=ATTN_BF16):
     return tuple(x.value for x in out)
 
 
-def set_policy(schedule: int = ATTN_SCHED_DEFAULT, qb: int = 1, nw: int = 8, ns: int = 4):
-    """Process-wide choice of the f16/bf16 schedule and tile shape (tuning and tests);
-    ATTN_SCHED_DEFAULT restores the measured policy table."""
-    _check(load_library().attn_fwd_set_policy(int(schedule), int(qb), int(nw), int(ns)))
+def set_policy(schedule: int = ATTN_SCHED_DEFAULT, qb: int = 1, nw: int = 8, ns: int = 4, bk: int = 64):
+    """Process-wide choice of the f16/bf16 schedule and tile shape: qb 32-query blocks per wave,
+    nw waves, ns LDS stages, bk keys per tile (tuning and tests); ATTN_SCHED_DEFAULT restores the
+    measured policy table."""
+    _check(load_library().attn_fwd_set_policy(int(schedule), int(qb), int(nw), int(ns), int(bk)))
 
 
 KERNEL_NAMES = {ATTN_SCHED_CLASSIC: "attn_fwd_kernel", ATTN_SCHED_PINGPONG: "attn_fwd_pp_kernel",

@@ -1344,7 +1344,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
 
 struct Plan {
     int sched;                   // ATTN_SCHED_CLASSIC, _PINGPONG or _DEPHASED (f16/bf16); 0 for fp8
-    int qb, nw, ns;              // 32-query blocks per wave, waves, LDS stages
+    int qb, nw, ns, bk;          // 32-query blocks per wave, waves, LDS stages, keys per tile
     int block_q, block_k, nqt, num_wg;
 };
 
@@ -1362,56 +1362,72 @@ int check_common(const void *q, const void *k, const void *v, const void *o, con
     return ATTN_OK;
 }
 
-// Schedules and tile shapes that are compiled: (schedule, query blocks per wave, waves, stages).
-constexpr int kShapes[][4] = {{ATTN_SCHED_CLASSIC, 1, 8, 3},  {ATTN_SCHED_CLASSIC, 1, 8, 4},
-                              {ATTN_SCHED_CLASSIC, 2, 4, 3},  {ATTN_SCHED_CLASSIC, 2, 4, 4},
-                              {ATTN_SCHED_CLASSIC, 1, 4, 2},  {ATTN_SCHED_CLASSIC, 1, 4, 3},
-                              {ATTN_SCHED_PINGPONG, 1, 8, 3}, {ATTN_SCHED_DEPHASED, 1, 8, 4},
-                              {ATTN_SCHED_CLASSIC, 2, 8, 3},  {ATTN_SCHED_CLASSIC, 2, 8, 4}};
+// Schedules and tile shapes that are compiled: (schedule, query blocks per wave, waves, stages,
+// keys per tile).
+constexpr int kShapes[][5] = {
+    {ATTN_SCHED_CLASSIC, 1, 8, 3, 64},  {ATTN_SCHED_CLASSIC, 1, 8, 4, 64},  {ATTN_SCHED_CLASSIC, 2, 4, 3, 64},
+    {ATTN_SCHED_CLASSIC, 2, 4, 4, 64},  {ATTN_SCHED_CLASSIC, 1, 4, 2, 64},  {ATTN_SCHED_CLASSIC, 1, 4, 3, 64},
+    {ATTN_SCHED_CLASSIC, 2, 8, 3, 64},  {ATTN_SCHED_CLASSIC, 2, 8, 4, 64},  {ATTN_SCHED_CLASSIC, 1, 8, 2, 128},
+    {ATTN_SCHED_PINGPONG, 1, 8, 3, 64}, {ATTN_SCHED_DEPHASED, 1, 8, 4, 64}};
 // (2, 8, *) holds 64 queries per wave at two waves per SIMD, which fits the registers at d = 64
-// only; at d = 128 a launch with it returns ATTN_ERR_UNSUPPORTED.
+// only; at d = 128 plans and launches with it return ATTN_ERR_UNSUPPORTED.  128-key tiles take
+// 64 KiB of LDS per stage at d = 128, so two stages; 192 or more keys per tile would not fit two
+// waves' registers per SIMD.
 
-bool compiled_shape(int sched, int qb, int nw, int ns) {
+bool compiled_shape(int sched, int qb, int nw, int ns, int bk) {
     for (const auto &sh : kShapes)
-        if (sh[0] == sched && sh[1] == qb && sh[2] == nw && sh[3] == ns) return true;
+        if (sh[0] == sched && sh[1] == qb && sh[2] == nw && sh[3] == ns && sh[4] == bk) return true;
     return false;
 }
 
+int pack_policy(int sched, int qb, int nw, int ns, int bk) {
+    return sched | (qb << 4) | (nw << 8) | (ns << 12) | ((bk / 64) << 16);
+}
+
 // Process-wide override of the policy table (attn_fwd_set_policy, or ATTN_FWD_POLICY =
-// "sched,qb,nw,ns" read once at the first call); sched 0 means none.
-std::atomic<int> g_override{-1};   // packed sched | qb << 8 | nw << 16 | ns << 24; -1: not read yet
+// "sched,qb,nw,ns,bk" read once at the first call); 0 means none, -1 not read yet.
+std::atomic<int> g_override{-1};
 
 int policy_override() {
     int v = g_override.load(std::memory_order_relaxed);
     if (v != -1) return v;
     int packed = 0;
     const char *e = std::getenv("ATTN_FWD_POLICY");
-    int a = 0, b = 0, c = 0, d = 0;
-    if (e && std::sscanf(e, "%d,%d,%d,%d", &a, &b, &c, &d) == 4 && compiled_shape(a, b, c, d))
-        packed = a | (b << 8) | (c << 16) | (d << 24);
+    int a = 0, b = 0, c = 0, d = 0, k = 0;
+    if (e && std::sscanf(e, "%d,%d,%d,%d,%d", &a, &b, &c, &d, &k) == 5 && compiled_shape(a, b, c, d, k))
+        packed = pack_policy(a, b, c, d, k);
     int expected = -1;
     g_override.compare_exchange_strong(expected, packed);
     return g_override.load(std::memory_order_relaxed);
 }
 
-// Tile policy, measured on MI355X (bf16, B=2 H=16 S=4096, B=4 H=16 S=2048 and causal B=1 H=32
-// S=8192 at d=128; causal B=1 H=16 S=16384 and B=1 H=2 S=128 at d=64): at d=128 the de-phased
-// schedule is 1.5-2% faster than the classic one; at d=64 it is 3% slower, and the classic
-// schedule with 64 queries per wave (2, 8, 4) is 7% faster than with 32 (1, 8, 4) as long as its
-// 512-query workgroups fill the 256 CUs (slower on the tiny S=128 workload, which they do not).
+// Tile policy, measured on MI355X (bf16 B=2 H=16 S=4096, B=4 H=16 S=2048 and causal B=1 H=32
+// S=8192 at d=128; causal B=1 H=16 S=16384 and B=1 H=2 S=128 at d=64).  d=128: the classic
+// schedule with 128-key tiles and two stages is 1.4-2.1% faster than the de-phased schedule on
+// 64-key tiles, which in turn is 1.5-2% faster than the classic schedule on 64-key tiles.  d=64:
+// the classic schedule with 64 queries per wave (2, 8, 4) is 7% faster than with 32 (1, 8, 4) as
+// long as its 512-query workgroups fill the 256 CUs (slower on the tiny S=128 workload, which
+// they do not); 128-key tiles and the de-phased schedule are not faster there.
 void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
     (void)causal;
-    pl->sched = d == 128 ? ATTN_SCHED_DEPHASED : ATTN_SCHED_CLASSIC;
+    pl->sched = ATTN_SCHED_CLASSIC;
     pl->qb = 1;
     pl->nw = 8;
-    pl->ns = 4;
-    if (d == 64 && (long long)B * H * ((Sq + 511) / 512) >= 256) pl->qb = 2;
+    if (d == 128) {
+        pl->ns = 2;
+        pl->bk = 128;
+    } else {
+        pl->ns = 4;
+        pl->bk = 64;
+        if ((long long)B * H * ((Sq + 511) / 512) >= 256) pl->qb = 2;
+    }
     const int ov = policy_override();
     if (ov > 0) {
-        pl->sched = ov & 255;
-        pl->qb = (ov >> 8) & 255;
-        pl->nw = (ov >> 16) & 255;
-        pl->ns = (ov >> 24) & 255;
+        pl->sched = ov & 15;
+        pl->qb = (ov >> 4) & 15;
+        pl->nw = (ov >> 8) & 15;
+        pl->ns = (ov >> 12) & 15;
+        pl->bk = ((ov >> 16) & 15) * 64;
     }
 }
 
@@ -1419,7 +1435,7 @@ int make_plan(int B, int H, int Sq, int d, int causal, Plan *pl) {
     choose_policy(B, H, Sq, d, causal, pl);
     if (pl->qb == 2 && pl->nw == 8 && d != 64) return ATTN_ERR_UNSUPPORTED;   // registers: d = 64 only
     pl->block_q = pl->nw * pl->qb * 32;
-    pl->block_k = 64;
+    pl->block_k = pl->bk;
     pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
     const long long wg = (long long)pl->nqt * B * H;
     if (wg > INT_MAX) return ATTN_ERR_OVERFLOW;
@@ -1427,9 +1443,9 @@ int make_plan(int B, int H, int Sq, int d, int causal, Plan *pl) {
     return ATTN_OK;
 }
 
-template <class T, int D, bool CAUSAL, int QB, int NW, int NS>
+template <class T, int D, bool CAUSAL, int QB, int NW, int NS, int BC = 64>
 int launch(const Params &p, const Plan &pl, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, NW, 64, NS, CAUSAL>), dim3(pl.num_wg), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, NW, BC, NS, CAUSAL>), dim3(pl.num_wg), dim3(NW * 64), 0, stream, p);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -1442,6 +1458,10 @@ int launch_shape(const Params &p, const Plan &pl, hipStream_t s) {
     if (pl.sched == ATTN_SCHED_DEPHASED) {
         hipLaunchKernelGGL((attn_fwd_dp_kernel<T, D, CAUSAL>), dim3(pl.num_wg), dim3(512), 0, s, p);
         return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    }
+    if (pl.bk == 128) {
+        if (pl.qb == 1 && pl.nw == 8 && pl.ns == 2) return launch<T, D, CAUSAL, 1, 8, 2, 128>(p, pl, s);
+        return ATTN_ERR_UNSUPPORTED;
     }
     const int key = pl.qb * 100 + pl.nw * 10 + pl.ns;
     switch (key) {
@@ -1472,6 +1492,7 @@ constexpr int kFp8Stages = 3;
 
 void make_plan_fp8(int B, int H, int Sq, Plan *pl) {
     pl->sched = 0;
+    pl->bk = 128;
     pl->qb = 1;
     pl->nw = 8;
     pl->ns = kFp8Stages;
@@ -1611,15 +1632,15 @@ extern "C" int attn_fwd_schedule(int d, int causal, int dtype) {
     return pl.sched;
 }
 
-extern "C" int attn_fwd_set_policy(int schedule, int qb, int nw, int ns) {
+extern "C" int attn_fwd_set_policy(int schedule, int qb, int nw, int ns, int bk) {
     if (schedule == 0) {
         policy_override();   // consume the environment once, then clear
         g_override.store(0, std::memory_order_relaxed);
         return ATTN_OK;
     }
-    if (!compiled_shape(schedule, qb, nw, ns)) return ATTN_ERR_UNSUPPORTED;
+    if (!compiled_shape(schedule, qb, nw, ns, bk)) return ATTN_ERR_UNSUPPORTED;
     policy_override();
-    g_override.store(schedule | (qb << 8) | (nw << 16) | (ns << 24), std::memory_order_relaxed);
+    g_override.store(pack_policy(schedule, qb, nw, ns, bk), std::memory_order_relaxed);
     return ATTN_OK;
 }
 

@@ -163,18 +163,20 @@ typedef enum {
 /*
  * Tuning and test hook: makes every later f16/bf16 attn_fwd call of this
  * process use one compiled schedule and tile shape (qb 32-query blocks per
- * wave, nw waves per workgroup, ns LDS stages) instead of the measured policy
- * table.  Compiled: CLASSIC (1,8,3) (1,8,4) (2,4,3) (2,4,4) (1,4,2) (1,4,3),
- * and for d = 64 only (2,8,3) (2,8,4) (attn_fwd then returns
- * ATTN_ERR_UNSUPPORTED at d = 128); PINGPONG (1,8,3); DEPHASED (1,8,4).
- * schedule = ATTN_SCHED_DEFAULT restores
- * the table (the other arguments are then ignored).  The environment variable
- * ATTN_FWD_POLICY="schedule,qb,nw,ns", read at the first call, sets the same
- * override.  Process-wide, not tied to a stream: calls in flight keep the
- * shape they were launched with.  Returns ATTN_OK, or ATTN_ERR_UNSUPPORTED
- * for a shape that is not compiled (the setting is then unchanged).
+ * wave, nw waves per workgroup, ns LDS stages, bk keys per tile) instead of
+ * the measured policy table.  Compiled, as (qb, nw, ns, bk):
+ *   CLASSIC   (1,8,3,64) (1,8,4,64) (2,4,3,64) (2,4,4,64) (1,4,2,64)
+ *             (1,4,3,64) (1,8,2,128), and for d = 64 only (2,8,3,64)
+ *             (2,8,4,64) (attn_fwd returns ATTN_ERR_UNSUPPORTED at d = 128);
+ *   PINGPONG  (1,8,3,64);  DEPHASED (1,8,4,64).
+ * schedule = ATTN_SCHED_DEFAULT restores the table (the other arguments are
+ * then ignored).  The environment variable ATTN_FWD_POLICY =
+ * "schedule,qb,nw,ns,bk", read at the first call, sets the same override.
+ * Process-wide, not tied to a stream: calls in flight keep the shape they
+ * were launched with.  Returns ATTN_OK, or ATTN_ERR_UNSUPPORTED for a shape
+ * that is not compiled (the setting is then unchanged).
  */
-int attn_fwd_set_policy(int schedule, int qb, int nw, int ns);
+int attn_fwd_set_policy(int schedule, int qb, int nw, int ns, int bk);
 
 /*
  * The schedule that attn_fwd launches for head dimension d, causal flag and

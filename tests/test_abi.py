@@ -141,31 +141,33 @@ def test_quantize_validation(lib):
     assert callq(lib, B=2 ** 16, H=2 ** 16, S=2 ** 10) == OVERFLOW
 
 
-COMPILED = [(ea.ATTN_SCHED_CLASSIC, 1, 8, 3), (ea.ATTN_SCHED_CLASSIC, 1, 8, 4), (ea.ATTN_SCHED_CLASSIC, 2, 4, 3),
-            (ea.ATTN_SCHED_CLASSIC, 2, 4, 4), (ea.ATTN_SCHED_CLASSIC, 1, 4, 2), (ea.ATTN_SCHED_CLASSIC, 1, 4, 3),
-            (ea.ATTN_SCHED_PINGPONG, 1, 8, 3), (ea.ATTN_SCHED_DEPHASED, 1, 8, 4)]
-D64_ONLY = [(ea.ATTN_SCHED_CLASSIC, 2, 8, 3), (ea.ATTN_SCHED_CLASSIC, 2, 8, 4)]
+C, PP, DP = ea.ATTN_SCHED_CLASSIC, ea.ATTN_SCHED_PINGPONG, ea.ATTN_SCHED_DEPHASED
+COMPILED = [(C, 1, 8, 3, 64), (C, 1, 8, 4, 64), (C, 2, 4, 3, 64), (C, 2, 4, 4, 64), (C, 1, 4, 2, 64),
+            (C, 1, 4, 3, 64), (C, 1, 8, 2, 128), (PP, 1, 8, 3, 64), (DP, 1, 8, 4, 64)]
+D64_ONLY = [(C, 2, 8, 3, 64), (C, 2, 8, 4, 64)]
 
 
 def test_set_policy(lib):
     try:
-        for bad in ((ea.ATTN_SCHED_CLASSIC, 3, 8, 4), (ea.ATTN_SCHED_PINGPONG, 1, 8, 4), (9, 1, 8, 4),
-                    (ea.ATTN_SCHED_DEPHASED, 1, 8, 3)):
+        for bad in ((C, 3, 8, 4, 64), (PP, 1, 8, 4, 64), (9, 1, 8, 4, 64), (DP, 1, 8, 3, 64), (C, 1, 8, 4, 128),
+                    (C, 1, 8, 2, 64), (C, 1, 8, 4, 192)):
             assert lib.attn_fwd_set_policy(*bad) == UNSUP
-        for sched, qb, nw, ns in COMPILED:
-            assert lib.attn_fwd_set_policy(sched, qb, nw, ns) == OK
+        for sched, qb, nw, ns, bkk in COMPILED:
+            assert lib.attn_fwd_set_policy(sched, qb, nw, ns, bkk) == OK
             bq, bk, w, n = ea.plan(2, 16, 4096, 4096, 128, False)
-            assert (bq, bk, w) == (qb * nw * 32, 64, nw) and n == -(-4096 // bq) * 32
+            assert (bq, bk, w) == (qb * nw * 32, bkk, nw) and n == -(-4096 // bq) * 32
             # fp8 plans do not follow the f16/bf16 override
             assert ea.plan(2, 16, 4096, 4096, 128, False, dtype=ea.ATTN_FP8_E4M3)[:3] == (256, 128, 8)
-        for sched, qb, nw, ns in D64_ONLY:
-            assert lib.attn_fwd_set_policy(sched, qb, nw, ns) == OK
+        for sched, qb, nw, ns, bkk in D64_ONLY:
+            assert lib.attn_fwd_set_policy(sched, qb, nw, ns, bkk) == OK
             assert ea.plan(1, 16, 4096, 4096, 64, False)[:3] == (512, 64, 8)
             with pytest.raises(ea.AttnError):
                 ea.plan(1, 16, 4096, 4096, 128, False)
     finally:
-        assert lib.attn_fwd_set_policy(ea.ATTN_SCHED_DEFAULT, 0, 0, 0) == OK
-    assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 64, 8)
+        assert lib.attn_fwd_set_policy(ea.ATTN_SCHED_DEFAULT, 0, 0, 0, 0) == OK
+    # the measured table: d = 128 takes 128-key tiles
+    assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 128, 8)
+    assert ea.kernel_name(128, False, ea.ATTN_BF16) == "attn_fwd_kernel"
     # d = 64: 64 queries per wave once the 512-query workgroups fill the 256 CUs
     assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (512, 64, 8)
     assert ea.plan(1, 2, 128, 128, 64, False)[:3] == (256, 64, 8)

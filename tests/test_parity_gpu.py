@@ -81,14 +81,15 @@ def test_small_full_e5m2(oracle, shape, causal):
     assert st["pass"], st
 
 
-SCHEDULES = [(1, 1, 8, 3), (1, 1, 8, 4), (1, 2, 4, 3), (1, 2, 4, 4), (1, 1, 4, 2), (1, 1, 4, 3), (2, 1, 8, 3),
-             (3, 1, 8, 4), (1, 2, 8, 3), (1, 2, 8, 4)]
-D64_ONLY = {(1, 2, 8, 3), (1, 2, 8, 4)}
+SCHEDULES = [(1, 1, 8, 3, 64), (1, 1, 8, 4, 64), (1, 2, 4, 3, 64), (1, 2, 4, 4, 64), (1, 1, 4, 2, 64),
+             (1, 1, 4, 3, 64), (1, 1, 8, 2, 128), (2, 1, 8, 3, 64), (3, 1, 8, 4, 64), (1, 2, 8, 3, 64),
+             (1, 2, 8, 4, 64)]
+D64_ONLY = {(1, 2, 8, 3, 64), (1, 2, 8, 4, 64)}
 SCHED_SHAPES = [(1, 1, 1, 1, 64), (1, 2, 17, 3, 128), (2, 3, 130, 130, 64), (1, 2, 300, 333, 128),
                 (1, 2, 513, 257, 128), (1, 2, 1000, 1000, 64)]
 
 
-@pytest.mark.parametrize("sched", SCHEDULES, ids=lambda s: "s%d_%d_%d_%d" % s)
+@pytest.mark.parametrize("sched", SCHEDULES, ids=lambda s: "s%d_%d_%d_%d_%d" % s)
 def test_every_schedule(oracle, sched):
     """Every compiled schedule and tile shape (not only the policy table's choice), bf16 and f16,
     causal and not, on ragged shapes at both head dimensions."""
