@@ -34,8 +34,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: line comments, trailing spaces and blank lines removed, so
+    that an edit of comments alone does not invalidate counters taken on the same compiled code."""
+    code = []
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def counter_traffic(kernel: str, workload: str):

@@ -17,16 +17,21 @@
 //     halves;
 //   * O^T = V^T P^T with the same MFMA: the S^T accumulator, rounded to the
 //     input type, is already the B operand (P never leaves registers); V^T is
-//     the A operand, read from an LDS copy of the V tile that is stored
-//     transposed with the key order of the accumulator layout;
-//   * K/V tiles are double-buffered in LDS: the global loads of tile t+1 are
-//     issued before the MFMA work on tile t and written to the other LDS buffer
-//     after it, one barrier per tile;
+//     the A operand, fetched from the row-major V tile in LDS with transposing
+//     reads (ds_read_b64_tr_b16);
+//   * K/V tiles reach LDS by direct-to-LDS loads (global_load_lds_dwordx4) into
+//     a ring of NS stages, NS-1 tiles ahead, with one explicit memory-counter
+//     wait and one barrier per tile;
 //   * exp2 with log2(e) folded into the scale (the page's section 4 computes the
-//     exponent in base 2);
+//     exponent in base 2); lazy rescaling of O;
 //   * causal: tiles wholly above the diagonal are never loaded; the mask is
 //     applied only on diagonal and tail tiles; query tiles are dispatched
 //     heaviest first and all tiles of one head land on one XCD.
+//
+// Kernels: attn_fwd_kernel (the schedule above; the policy table's choice at both
+// head dims), attn_fwd_dp_kernel (SIMD partner waves one softmax apart) and
+// attn_fwd_pp_kernel (barrier-separated ping-pong), both opt-in; attn_fwd_fp8_kernel
+// (block-scaled E4M3 / E5M2).  The host side at the end holds the policy table.
 #include <hip/hip_runtime.h>
 
 #include <climits>
