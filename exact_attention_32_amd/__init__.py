@@ -119,23 +119,24 @@ def _stream(dev):
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: float | None = None,
         out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
-    """Exact attention forward for fp16 / bf16 tensors [B, H, S, d] -> (O, LSE).
+    """Exact attention forward for tensors [B, H, S, d] -> (O, LSE).
 
-    O has q's dtype; LSE is fp32 [B, H, S_q] (natural log), or None if want_lse is False.
+    fp16 / bf16: O has q's dtype.  float8_e4m3fn / float8_e5m2 (fp8 codes with unit descales; see
+    fwd_fp8 for block-scaled codes): O is bf16.  LSE is fp32 [B, H, S_q] (natural log), or None if
+    want_lse is False.
     """
     B, H, S_q, S_k, d = _shapes(q, k, v)
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share a dtype")
-    if q.dtype == torch.bfloat16:
-        dt = ATTN_BF16
-    elif q.dtype == torch.float16:
-        dt = ATTN_F16
-    else:
+    dt = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16, torch.float8_e4m3fn: ATTN_FP8_E4M3,
+          torch.float8_e5m2: ATTN_FP8_E5M2}.get(q.dtype)
+    if dt is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if scale is None:
         scale = d ** -0.5
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if dt in (ATTN_FP8_E4M3, ATTN_FP8_E5M2) else q.dtype,
+                          device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
     rc = load_library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

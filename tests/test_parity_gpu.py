@@ -203,3 +203,27 @@ def test_fp8_quantisation_error_report(oracle, name):
     U.say(f"   vs unquantised fp32 inputs: max|dO| {err_o.max():.3e} rms {np.sqrt((err_o ** 2).mean()):.3e}, "
           f"max|dLSE| {err_l.max():.3e}")
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_unit_descales(oracle, fmt, causal):
+    """fp8 codes through attn_fwd (unit descales) equal fwd_fp8 with all-one descales, bit for bit,
+    and match the oracle on the decoded codes."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    B, H, S, d = 1, 2, 333, 128
+    U.say(f"[gpu] fp8 unit descales {fmt} causal={causal}")
+    q, k, v, _ = I.make_device_inputs(B, H, S, d, "fp8" if fmt == "e4m3" else "e5m2", seed=21 + causal)
+    tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    o1, l1 = ea.fwd(q.view(tdt), k.view(tdt), v.view(tdt), causal=causal)
+    ones = torch.ones((B, H, (S + 127) // 128), dtype=torch.float32, device=dev)
+    o2, l2 = ea.fwd_fp8(q, k, v, ones, ones, ones, causal=causal, fmt=fmt)
+    torch.cuda.synchronize()
+    assert o1.dtype == torch.bfloat16 and torch.equal(o1, o2) and torch.equal(l1, l2)
+    dec = [oracle.decode_fp8_blocks(t.cpu().numpy(), ones.cpu().numpy(), fmt) for t in (q, k, v)]
+    ro, rl = oracle.attention(*dec, causal, d ** -0.5)
+    st = U.compare(o1.double().cpu().numpy(), l1.double().cpu().numpy(), ro, rl, "fp8")
+    U.say(f"   {st}")
+    assert st["pass"], st
