@@ -1354,17 +1354,22 @@ struct Plan {
     int block_q, block_k, nqt, num_wg;
 };
 
+// Internal status of check_common: no query rows (B, H or S_q = 0), so nothing to compute.
+constexpr int kEmpty = -1;
+
 int check_common(const void *q, const void *k, const void *v, const void *o, const void *lse, int B, int H, int Sq,
                  int Sk, int d, float scale) {
-    if (!q || !k || !v || !o) return ATTN_ERR_NULL;
-    if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SHAPE;
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_VALUE;
+    if (B == 0 || H == 0 || Sq == 0) return kEmpty;
+    if (Sk == 0) return ATTN_ERR_SHAPE;   // a softmax over no keys is undefined
+    if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     const uintptr_t mis = (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                            reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) & 15u;
     if (mis || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
     if ((long long)Sq * d > INT_MAX || (long long)Sk * d > INT_MAX || (long long)B * H > INT_MAX)
         return ATTN_ERR_OVERFLOW;
-    if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_VALUE;
     return ATTN_OK;
 }
 
@@ -1563,12 +1568,14 @@ int check_descales(const float *q_descale, const float *k_descale, const float *
 
 extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S_q,
                         int S_k, int d, int causal, float scale, int dtype, void *stream) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3 && dtype != ATTN_FP8_E5M2)
+        return ATTN_ERR_UNSUPPORTED;
     int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
+    if (st == kEmpty) return ATTN_OK;
     if (st != ATTN_OK) return st;
     if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2)
         return run_fp8(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, S_q, S_k, d, causal, scale,
                        dtype == ATTN_FP8_E5M2 ? 1 : 0, stream);
-    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     Plan pl;
     st = make_plan(B, H, S_q, d, causal, &pl);
     if (st != ATTN_OK) return st;
@@ -1593,6 +1600,7 @@ extern "C" int attn_fwd_fp8(const void *q, const void *k, const void *v, const f
                             const float *k_descale, const float *v_descale, void *o, float *lse, int B, int H,
                             int S_q, int S_k, int d, int causal, float scale, void *stream) {
     int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
+    if (st == kEmpty) return ATTN_OK;
     if (st != ATTN_OK) return st;
     st = check_descales(q_descale, k_descale, v_descale);
     if (st != ATTN_OK) return st;
@@ -1603,6 +1611,7 @@ extern "C" int attn_fwd_fp8_e5m2(const void *q, const void *k, const void *v, co
                                  const float *k_descale, const float *v_descale, void *o, float *lse, int B, int H,
                                  int S_q, int S_k, int d, int causal, float scale, void *stream) {
     int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
+    if (st == kEmpty) return ATTN_OK;
     if (st != ATTN_OK) return st;
     st = check_descales(q_descale, k_descale, v_descale);
     if (st != ATTN_OK) return st;
@@ -1611,12 +1620,22 @@ extern "C" int attn_fwd_fp8_e5m2(const void *q, const void *k, const void *v, co
 
 extern "C" int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, int dtype, int *block_q,
                              int *block_k, int *waves, int *workgroups) {
-    if (B < 1 || H < 1 || S_q < 1 || S_k < 1) return ATTN_ERR_SHAPE;
+    if (B < 0 || H < 0 || S_q < 0 || S_k < 0) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3 && dtype != ATTN_FP8_E5M2)
         return ATTN_ERR_UNSUPPORTED;
+    const bool empty = B == 0 || H == 0 || S_q == 0;   // no query rows: a plan with no workgroups
+    if (!empty && S_k == 0) return ATTN_ERR_SHAPE;
     Plan pl;
-    if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2) {
+    if (empty) {
+        if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2) {
+            make_plan_fp8(1, 1, 1, &pl);
+        } else {
+            const int st = make_plan(1, 1, 1, d, causal, &pl);
+            if (st != ATTN_OK) return st;
+        }
+        pl.num_wg = 0;
+    } else if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2) {
         make_plan_fp8(B, H, S_q, &pl);
         if (pl.num_wg == 0) return ATTN_ERR_OVERFLOW;
     } else {
@@ -1655,7 +1674,7 @@ extern "C" const char *attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL: return "a required pointer (q, k, v or o) is NULL";
-        case ATTN_ERR_SHAPE: return "B, H, S_q and S_k must be >= 1";
+        case ATTN_ERR_SHAPE: return "a size is negative, or S_k is 0 while there are queries";
         case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128) or dtype";
         case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case ATTN_ERR_OVERFLOW: return "S*d or the workgroup count exceeds the 32-bit index range";

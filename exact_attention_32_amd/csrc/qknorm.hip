@@ -152,16 +152,19 @@ int launch_qn(const QnParams &p, int d, int nwg, hipStream_t s) {
 extern "C" int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, const void *w_k, void *q_out,
                                void *k_out, int B, int H, int S_q, int S_k, int d, float eps, int dtype,
                                void *stream) {
-    if (!q || !k || !w_q || !w_k || !q_out || !k_out) return ATTN_ERR_NULL;
-    if (B < 1 || H < 1 || S_q < 1 || S_k < 1) return ATTN_ERR_SHAPE;
+    if (B < 0 || H < 0 || S_q < 0 || S_k < 0) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
     if ((long long)H * d > 64LL * 8 * QN_MAXG) return ATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(eps) || eps < 0.f) return ATTN_ERR_VALUE;
+    if (B == 0 || H == 0 || (S_q == 0 && S_k == 0)) return ATTN_OK;   // no tokens: nothing to do
+    // a tensor with no tokens is not read or written: its pointers may be NULL
+    if (S_q > 0 && (!q || !w_q || !q_out)) return ATTN_ERR_NULL;
+    if (S_k > 0 && (!k || !w_k || !k_out)) return ATTN_ERR_NULL;
     const uintptr_t mis = (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                            reinterpret_cast<uintptr_t>(w_q) | reinterpret_cast<uintptr_t>(w_k) |
                            reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(k_out)) & 15u;
     if (mis) return ATTN_ERR_ALIGN;
-    if (!std::isfinite(eps) || eps < 0.f) return ATTN_ERR_VALUE;
     const long long tq = (long long)B * S_q, tk = (long long)B * S_k;
     const long long tmax = tq > tk ? tq : tk;
     if (tmax > INT_MAX || (long long)B * H > INT_MAX || (long long)S_q * d > INT_MAX || (long long)S_k * d > INT_MAX)

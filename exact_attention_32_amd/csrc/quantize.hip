@@ -203,11 +203,13 @@ int launch_quant(const QuantParams &qp, int ntensors, int dtype, hipStream_t s) 
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-// argument checks of one tensor; fills slot i of qp
+// argument checks of one tensor; fills slot i of qp (an empty tensor, B, H or S = 0, leaves the
+// slot with no workgroups, and its pointers are not used)
 int check_tensor(const void *x, void *codes, float *descale, int B, int H, int S, QuantParams *qp, int i) {
+    if (B < 0 || H < 0 || S < 0) return ATTN_ERR_SHAPE;
+    if (B == 0 || H == 0 || S == 0) return ATTN_OK;
     if (!x || !codes) return ATTN_ERR_NULL;
     if (!descale) return ATTN_ERR_DESCALE;
-    if (B < 1 || H < 1 || S < 1) return ATTN_ERR_SHAPE;
     if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes)) & 15u) return ATTN_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(descale) & 3u) return ATTN_ERR_DESCALE;
     const long long nblk = (S + QBLK - 1) / QBLK;
@@ -222,9 +224,16 @@ int check_tensor(const void *x, void *codes, float *descale, int B, int H, int S
     return ATTN_OK;
 }
 
-int launch_checked(const QuantParams &qp, int ntensors, int dtype, int d, int fmt, void *stream) {
+int check_types(int dtype, int d) {
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+int launch_checked(const QuantParams &qp, int ntensors, int dtype, int d, int fmt, void *stream) {
+    int any = 0;
+    for (int i = 0; i < ntensors; ++i) any |= qp.nwg[i];
+    if (!any) return ATTN_OK;   // every tensor is empty: nothing to launch
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fmt == 0)
         return d == 128 ? launch_quant<128, 0>(qp, ntensors, dtype, s) : launch_quant<64, 0>(qp, ntensors, dtype, s);
@@ -233,8 +242,10 @@ int launch_checked(const QuantParams &qp, int ntensors, int dtype, int d, int fm
 
 template <int FMT>
 int quantize(const void *x, int dtype, void *codes, float *descale, int B, int H, int S, int d, void *stream) {
+    int st = check_types(dtype, d);
+    if (st != ATTN_OK) return st;
     QuantParams qp = {};
-    const int st = check_tensor(x, codes, descale, B, H, S, &qp, 0);
+    st = check_tensor(x, codes, descale, B, H, S, &qp, 0);
     if (st != ATTN_OK) return st;
     return launch_checked(qp, 1, dtype, d, FMT, stream);
 }
@@ -255,8 +266,10 @@ extern "C" int attn_quantize_qkv(const void *q, const void *k, const void *v, in
                                  void *k_codes, void *v_codes, float *q_descale, float *k_descale, float *v_descale,
                                  int B, int H, int S_q, int S_k, int d, void *stream) {
     if (fmt != ATTN_FP8_E4M3 && fmt != ATTN_FP8_E5M2) return ATTN_ERR_UNSUPPORTED;
+    int st = check_types(dtype, d);
+    if (st != ATTN_OK) return st;
     QuantParams qp = {};
-    int st = check_tensor(q, q_codes, q_descale, B, H, S_q, &qp, 0);
+    st = check_tensor(q, q_codes, q_descale, B, H, S_q, &qp, 0);
     if (st == ATTN_OK) st = check_tensor(k, k_codes, k_descale, B, H, S_k, &qp, 1);
     if (st == ATTN_OK) st = check_tensor(v, v_codes, v_descale, B, H, S_k, &qp, 2);
     if (st != ATTN_OK) return st;

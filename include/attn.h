@@ -23,7 +23,13 @@
  * results are deterministic (no atomics).
  *
  * Errors: every argument is checked on the host before anything is enqueued;
- * on any error nothing is launched and o/lse are untouched.  The guards follow
+ * on any error nothing is launched and o/lse are untouched.
+ *
+ * Empty inputs: sizes may be 0.  A call with no query rows (B, H or S_q = 0)
+ * checks d, dtype and scale, then returns ATTN_OK without launching, reading
+ * or writing anything (its pointers may then be NULL).  S_k = 0 while there
+ * are query rows is ATTN_ERR_SHAPE: a softmax over no keys is undefined.  The
+ * quantisers and the RMSNorm likewise do nothing for a tensor with no rows.  The guards follow
  * the host-side checks that the FlashInfer KDA write-up (blog.secrett2633)
  * describes in its section 3 (16-byte base alignment, 32-bit index range).
  */
@@ -45,7 +51,7 @@ typedef enum {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,         /* q, k, v or o is NULL (lse may be NULL: then it is not written) */
-    ATTN_ERR_SHAPE = 2,        /* B, H, S_q or S_k < 1 */
+    ATTN_ERR_SHAPE = 2,        /* a size < 0, or S_k = 0 while there are query rows */
     ATTN_ERR_UNSUPPORTED = 3,  /* d not 64 or 128, or unknown dtype */
     ATTN_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
     ATTN_ERR_OVERFLOW = 5,     /* S*d or the grid size exceeds the 32-bit index range */
@@ -129,7 +135,8 @@ int attn_quantize_e5m2(const void *x, int dtype, void *codes, float *descale, in
  *   q        : [B][H][S_q][d], k and v: [B][H][S_k][d], all of type dtype
  *   *_codes  : uint8, the inputs' shapes; *_descale: fp32 [B][H][ceil(S/128)]
  * Results are bit-identical to the three single-tensor calls.  Argument
- * checks, errors and ownership as for attn_quantize_e4m3.
+ * checks, errors and ownership as for attn_quantize_e4m3; a tensor with no
+ * rows (S_q = 0, or S_k = 0) is skipped and its pointers may be NULL.
  */
 int attn_quantize_qkv(const void *q, const void *k, const void *v, int dtype, int fmt, void *q_codes, void *k_codes,
                       void *v_codes, float *q_descale, float *k_descale, float *v_descale, int B, int H, int S_q,
@@ -147,7 +154,8 @@ int attn_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  *   eps       : finite, >= 0;  d: 64 or 128;  H*d <= 8192
  * In place is allowed (q_out == q and/or k_out == k); other overlaps are
  * undefined.  All pointers 16-byte aligned.  The outputs are attn_fwd's q and
- * k.  Returns an attn_status.
+ * k.  A tensor with no tokens (S_q = 0, or S_k = 0) is not touched and its
+ * three pointers may be NULL.  Returns an attn_status.
  */
 int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, const void *w_k, void *q_out, void *k_out,
                     int B, int H, int S_q, int S_k, int d, float eps, int dtype, void *stream);
@@ -192,8 +200,8 @@ const char *attn_status_string(int status);
 /*
  * Tile shape the library launches for a problem (for reports and tests):
  * writes queries per workgroup, keys per tile, waves per workgroup and the
- * workgroup count.  Returns an attn_status (argument checks as attn_fwd, no
- * device access).
+ * workgroup count (0 when there are no query rows).  Returns an attn_status
+ * (argument checks as attn_fwd, no device access).
  */
 int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, int dtype, int *block_q, int *block_k,
                   int *waves, int *workgroups);

@@ -70,9 +70,41 @@ def test_null_pointers(lib):
 
 def test_shapes(lib):
     for kw in ("B", "H", "Sq", "Sk"):
-        assert call(lib, **{kw: 0}) == SHAPE
         assert call(lib, **{kw: -3}) == SHAPE
-        assert call8(lib, **{kw: 0}) == SHAPE
+        assert call8(lib, **{kw: -1}) == SHAPE
+    # no keys while there are queries: the softmax is undefined
+    assert call(lib, Sk=0) == SHAPE and call8(lib, Sk=0) == SHAPE
+
+
+def test_empty_inputs(lib):
+    """No query rows: ATTN_OK with nothing launched, read or written (so NULL pointers are fine and
+    no GPU is needed); d, dtype and scale are still checked."""
+    none = dict(q=None, k=None, v=None, o=None, lse=None)
+    for kw in ("B", "H", "Sq"):
+        assert call(lib, **{kw: 0}) == OK
+        assert call(lib, **{kw: 0}, **none) == OK
+        assert call(lib, **{kw: 0}, Sk=0, **none) == OK
+        assert call8(lib, **{kw: 0}, qd=None, kd=None, vd=None, **none) == OK
+        for dt in (0, 1, 2, 4):
+            assert call(lib, **{kw: 0}, dtype=dt, **none) == OK
+        assert call(lib, **{kw: 0}, d=96) == UNSUP and call(lib, **{kw: 0}, dtype=7) == UNSUP
+        assert call(lib, **{kw: 0}, scale=0.0) == VALUE and call8(lib, **{kw: 0}, scale=float("nan")) == VALUE
+    bq, bk, w, n = ea.plan(0, 16, 4096, 4096, 128, False)
+    assert n == 0 and (bq, bk, w) == ea.plan(1, 1, 1, 1, 128, False)[:3]
+    assert ea.plan(2, 16, 0, 0, 64, True, dtype=ea.ATTN_FP8_E4M3)[3] == 0
+    with pytest.raises(ea.AttnError):
+        ea.plan(1, 1, 16, 0, 128)
+    # quantisers: a tensor with no rows is skipped
+    for kw in ("B", "H", "S"):
+        assert callq(lib, **{kw: 0}, x=None, codes=None, ds=None) == OK
+        assert callq(lib, **{kw: 0}, d=96) == UNSUP
+    assert callqkv(lib, B=0, q=None, k=None, v=None, cq=None, ck=None, cv=None, dq=None, dk=None, dv=None) == OK
+    assert callqkv(lib, Sq=0, Sk=0, dtype=2) == UNSUP
+    assert callqkv(lib, Sq=0, Sk=0, q=None, cq=None, dq=None) == OK
+    # QK-RMSNorm: no tokens, nothing to do
+    assert callqn(lib, B=0, q=None, k=None, wq=None, wk=None, qo=None, ko=None) == OK
+    assert callqn(lib, Sq=0, Sk=0, q=None, k=None, wq=None, wk=None, qo=None, ko=None) == OK
+    assert callqn(lib, B=0, eps=-1.0) == VALUE and callqn(lib, B=0, d=96) == UNSUP
 
 
 def test_unsupported(lib):
@@ -134,7 +166,7 @@ def test_quantize_validation(lib):
     assert callq(lib, x=None) == NULL and callq(lib, codes=None) == NULL
     assert callq(lib, ds=None) == DESCALE and callq(lib, ds=P + 2) == DESCALE
     for kw in ("B", "H", "S"):
-        assert callq(lib, **{kw: 0}) == SHAPE
+        assert callq(lib, **{kw: -1}) == SHAPE
     assert callq(lib, d=96) == UNSUP and callq(lib, dtype=2) == UNSUP and callq(lib, dtype=4) == UNSUP
     assert callq(lib, dtype=7) == UNSUP
     assert callq(lib, x=P + 4) == ALIGN and callq(lib, codes=P + 8) == ALIGN
@@ -182,7 +214,9 @@ def test_qk_rmsnorm_validation(lib):
         assert callqn(lib, **{kw: None}) == NULL
         assert callqn(lib, **{kw: P + 8}) == ALIGN
     for kw in ("B", "H", "Sq", "Sk"):
-        assert callqn(lib, **{kw: 0}) == SHAPE
+        assert callqn(lib, **{kw: -1}) == SHAPE
+    # a tensor with no tokens is not touched, so its pointers are not needed, but the other's are
+    assert callqn(lib, Sq=0, k=None) == NULL and callqn(lib, Sk=0, q=None) == NULL
     assert callqn(lib, d=96) == UNSUP and callqn(lib, dtype=2) == UNSUP and callqn(lib, dtype=3) == UNSUP
     assert callqn(lib, H=65, d=128) == UNSUP and callqn(lib, H=129, d=64) == UNSUP
     for e in (-1e-6, float("nan"), float("inf")):
@@ -202,7 +236,9 @@ def test_quantize_qkv_validation(lib):
     for kw in ("q", "k", "v", "cq", "ck", "cv"):
         assert callqkv(lib, **{kw: P + 4}) == ALIGN
     for kw in ("B", "H", "Sq", "Sk"):
-        assert callqkv(lib, **{kw: 0}) == SHAPE
+        assert callqkv(lib, **{kw: -1}) == SHAPE
+    # an empty tensor is skipped, but the others' pointers are still checked
+    assert callqkv(lib, Sq=0, k=None) == NULL and callqkv(lib, Sk=0, q=None) == NULL
     assert callqkv(lib, fmt=0) == UNSUP and callqkv(lib, fmt=1) == UNSUP and callqkv(lib, fmt=3) == UNSUP
     assert callqkv(lib, d=96) == UNSUP and callqkv(lib, dtype=2) == UNSUP
     assert callqkv(lib, B=2 ** 16, H=2 ** 16, Sk=2 ** 10) == OVERFLOW

@@ -227,3 +227,31 @@ def test_fp8_unit_descales(oracle, fmt, causal):
     st = U.compare(o1.double().cpu().numpy(), l1.double().cpu().numpy(), ro, rl, "fp8")
     U.say(f"   {st}")
     assert st["pass"], st
+
+
+def test_empty_queries(oracle):
+    """No query rows (B, H or S_q = 0): empty O and LSE, nothing launched; keys without queries are
+    fine, queries without keys are an error.  The sizes around the empty call stay correct."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    U.say("[gpu] empty inputs")
+    for B, H, S_q, S_k in ((1, 2, 0, 64), (0, 2, 16, 16), (1, 0, 16, 16), (1, 2, 0, 0)):
+        for dt in (torch.bfloat16, torch.float16):
+            q = torch.zeros(B, H, S_q, 128, dtype=dt, device=dev)
+            k = torch.zeros(B, H, S_k, 128, dtype=dt, device=dev)
+            o, lse = ea.fwd(q, k, k, causal=True)
+            assert o.shape == (B, H, S_q, 128) and lse.shape == (B, H, S_q)
+        q8 = torch.zeros(B, H, S_q, 64, dtype=torch.uint8, device=dev)
+        k8 = torch.zeros(B, H, S_k, 64, dtype=torch.uint8, device=dev)
+        ds = [torch.ones(B, H, (s + 127) // 128, device=dev) for s in (S_q, S_k, S_k)]
+        for fmt in ("e4m3", "e5m2"):
+            o, lse = ea.fwd_fp8(q8, k8, k8, *ds, fmt=fmt)
+            assert o.shape == (B, H, S_q, 64) and o.dtype == torch.bfloat16
+    with pytest.raises(ea.AttnError):
+        ea.fwd(torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16, device=dev),
+               torch.zeros(1, 1, 0, 64, dtype=torch.bfloat16, device=dev),
+               torch.zeros(1, 1, 0, 64, dtype=torch.bfloat16, device=dev))
+    # a normal call right after still matches the oracle
+    st = _run_full(oracle, I.random_workload(1, 2, 70, 90, 64, "bf16", True, seed=8))
+    assert st["pass"], st

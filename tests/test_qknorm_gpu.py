@@ -112,3 +112,21 @@ def test_qknorm_then_attention(oracle, shape, causal):
     st = U.compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "bf16")
     U.say(f"   {st}")
     assert st["pass"], st
+
+
+def test_qknorm_empty(oracle):
+    """A tensor with no tokens is not touched; the other one is normalised as usual."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    U.say("[gpu] qk_rmsnorm empty")
+    k, wk = _draw(1, 4, 37, 128, "bf16", 5)
+    q = torch.zeros(1, 4, 0, 128, dtype=torch.bfloat16, device=dev)
+    qn, kn = ea.qk_rmsnorm(q, k.to(dev), wk.to(dev), wk.to(dev), eps=1e-6)
+    torch.cuda.synchronize()
+    assert qn.shape == q.shape
+    ref = oracle.rmsnorm_across_heads(k.double().numpy(), wk.double().numpy(), 1e-6)
+    dist, frac = _ulp_close(kn, ref, "bf16")
+    assert dist <= 1 and frac <= 1e-3, (dist, frac)
+    e = torch.zeros(0, 4, 5, 128, dtype=torch.bfloat16, device=dev)
+    ea.qk_rmsnorm(e, e, wk.to(dev), wk.to(dev))

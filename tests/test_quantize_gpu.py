@@ -117,3 +117,24 @@ def test_quantize_qkv_equals_single_calls(oracle, fmt, dtype):
     for t, c, d in zip((q, k, v), codes, ds):
         c1, d1 = ea.quantize_fp8(t, fmt)
         assert torch.equal(c, c1) and torch.equal(d, d1)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quantize_empty(oracle, fmt):
+    """A tensor with no rows is skipped: empty outputs alone, and the other tensors of a Q, K, V
+    launch are quantised as by single calls."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    U.say(f"[gpu] quantize empty {fmt}")
+    for shape in ((2, 3, 0, 128), (0, 3, 50, 64), (2, 0, 50, 128)):
+        codes, ds = ea.quantize_fp8(torch.zeros(shape, device=dev), fmt)
+        assert codes.shape == shape and ds.shape == (shape[0], shape[1], (shape[2] + 127) // 128)
+    q = torch.zeros(2, 3, 0, 128, device=dev)
+    k = torch.from_numpy(_draw((2, 3, 300, 128), 14)).to(dev)
+    v = torch.from_numpy(_draw((2, 3, 300, 128), 15)).to(dev)
+    (qc, kc, vc), (qd, kd, vd) = ea.quantize_qkv(q, k, v, fmt)
+    assert qc.shape == q.shape and qd.shape == (2, 3, 0)
+    for t, c, d in ((k, kc, kd), (v, vc, vd)):
+        c1, d1 = ea.quantize_fp8(t, fmt)
+        assert torch.equal(c, c1) and torch.equal(d, d1)
