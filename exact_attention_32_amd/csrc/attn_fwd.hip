@@ -1219,16 +1219,27 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
         for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
-        static_for<KSTEPS>([&](auto KS) {
-            constexpr int ks = decltype(KS)::value;
-            static_for<BC / 32>([&](auto KB) {
-                constexpr int kb2 = decltype(KB)::value;
+        // S^T MFMAs in a fixed order, each fenced, with the K fetches of the next two in flight
+        // (0.5-1% faster than the compiler's order on the fp8 workloads; a ring of four was slower)
+        {
+            constexpr int NQK = KSTEPS * (BC / 32), RING = 2;
+            auto kread = [&](auto J) __attribute__((always_inline)) {
+                constexpr int jj = decltype(J)::value, ks = jj / (BC / 32), kb2 = jj % (BC / 32);
                 const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks]);
                 const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks + 1]);
-                const i32x8 a = __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                return __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            };
+            i32x8 ring[RING];
+            static_for<RING>([&](auto J) { ring[decltype(J)::value] = kread(J); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<NQK>([&](auto J) {
+                constexpr int jj = decltype(J)::value, ks = jj / (BC / 32), kb2 = jj % (BC / 32);
+                const i32x8 a = ring[jj % RING];
+                if constexpr (jj + RING < NQK) ring[jj % RING] = kread(std::integral_constant<int, jj + RING>{});
                 s[kb2] = mfma_f8<FMT, FMT>(a, qf[ks], s[kb2]);
+                __builtin_amdgcn_sched_barrier(0);
             });
-        });
+        }
         if (masked) {
             const int base = k0 + 4 * g;
             int lim = Sk - base;
