@@ -200,8 +200,10 @@ def test_set_policy(lib):
     # the measured table: d = 128 takes 128-key tiles
     assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 128, 8)
     assert ea.kernel_name(128, False, ea.ATTN_BF16) == "attn_fwd_kernel"
-    # d = 64: 64 queries per wave once the 512-query workgroups fill the 256 CUs
-    assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (512, 64, 8)
+    # d = 64: 64 queries per wave once the 512-query workgroups fill the 256 CUs; causal at that
+    # size, 128-key tiles with 32 queries per wave
+    assert ea.plan(1, 16, 16384, 16384, 64, False)[:3] == (512, 64, 8)
+    assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (256, 128, 8)
     assert ea.plan(1, 2, 128, 128, 64, False)[:3] == (256, 64, 8)
 
 
