@@ -22,6 +22,9 @@
 //   * K/V tiles reach LDS by direct-to-LDS loads (global_load_lds_dwordx4) into
 //     a ring of NS stages, NS-1 tiles ahead, with one explicit memory-counter
 //     wait and one barrier per tile;
+//   * each MFMA stream (S^T, then P.V) issues in a fixed order, one MFMA per
+//     scheduling fence, with the LDS operand fetches of the next few MFMAs in
+//     flight;
 //   * exp2 with log2(e) folded into the scale (the page's section 4 computes the
 //     exponent in base 2); lazy rescaling of O;
 //   * causal: tiles wholly above the diagonal are never loaded; the mask is
