@@ -204,7 +204,9 @@ def test_set_policy(lib):
     # size, 128-key tiles with 32 queries per wave
     assert ea.plan(1, 16, 16384, 16384, 64, False)[:3] == (512, 64, 8)
     assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (256, 128, 8)
-    assert ea.plan(1, 2, 128, 128, 64, False)[:3] == (256, 64, 8)
+    # at most 128 query rows: 128-query workgroups (no clamped rows computed)
+    assert ea.plan(1, 2, 128, 128, 64, False)[:3] == (128, 64, 4)
+    assert ea.plan(1, 2, 129, 128, 64, False)[:3] == (256, 64, 8)
 
 
 def callqn(lib, q=P, k=P, wq=P, wk=P, qo=P, ko=P, B=1, H=2, Sq=16, Sk=16, d=128, eps=1e-6, dtype=1):
