@@ -255,3 +255,48 @@ def test_empty_queries(oracle):
     # a normal call right after still matches the oracle
     st = _run_full(oracle, I.random_workload(1, 2, 70, 90, 64, "bf16", True, seed=8))
     assert st["pass"], st
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_graph_replay_equals_eager(oracle, dtype):
+    """The attention launch captured in a HIP graph (the library allocates nothing and records no
+    memset): three replays, with eager work and synchronisations between them, each bit-equal to
+    the eager result."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    U.say(f"[gpu] graph replay {dtype}")
+    w = I.random_workload(1, 4, 700, 900, 128, dtype, True, seed=31)
+    x = I.make_inputs(w)
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    o = torch.empty((w.B, w.H, w.S_q, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
+    if dtype == "fp8":
+        qd, kd, vd = x.q_descale.to(dev), x.k_descale.to(dev), x.v_descale.to(dev)
+
+        def run():
+            ea.fwd_fp8(q, k, v, qd, kd, vd, causal=True, scale=w.scale, out=o, lse=lse)
+    else:
+        def run():
+            ea.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+    run()
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        o.fill_(7.0)
+        lse.fill_(7.0)
+        junk = torch.randn(1024, 1024, device=dev) @ torch.randn(1024, 1024, device=dev)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {rep} differs from the eager result"
+        del junk
