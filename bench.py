@@ -207,6 +207,7 @@ def main(argv=None):
             "traffic": counter_traffic(kernel, work.name),
             "kernel": kernel,
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+            "median_launch_us": round(float(np.median(per_launch)) * 1e3, 2),
             "min_launch_us": round(float(np.min(per_launch)) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,
             "algorithmic_hbm_bytes_per_launch": work.hbm_bytes(),
