@@ -146,7 +146,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); every (b, h) head is "
+        print(f"bench.py: this library runs on one GPU only (--gpus {args.gpus} requested); every (b, h) head is "
               "independent, so sharding heads over GPUs needs no communication, but no multi-GPU path is built.",
               file=sys.stderr)
         return 2
