@@ -39,6 +39,9 @@ SMALL = [
     (1, 2, 513, 257, 128),
     (2, 1, 640, 640, 64),
     (1, 2, 1000, 1000, 128),
+    # at most 128 query rows (the small-problem workgroup shape) against many key tiles
+    (1, 2, 128, 700, 128),
+    (2, 2, 96, 1000, 64),
 ]
 
 
