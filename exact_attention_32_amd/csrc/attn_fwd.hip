@@ -96,7 +96,8 @@ template <> __device__ __forceinline__ float sum2<F16>(uint32_t a, float acc) {
 }
 
 // The running max moves only when a row's max would grow by more than RESCALE_LOG2 (base 2);
-// until then p = exp2(s*c - m) <= 2^RESCALE_LOG2 and the O rescale is skipped.
+// until then p = exp2(s*c - m) <= 2^RESCALE_LOG2 and the O rescale is skipped.  (The classic
+// kernel bounds the row sums instead, which it forms anyway.)
 constexpr float RESCALE_LOG2 = 8.0f;
 
 // Row max between lane l and lane l^32 (the two halves of a 32x32 accumulator column).
@@ -361,57 +362,101 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                         if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[qb][kb2][i] = -INFINITY;
             }
         }
-        // online softmax (base 2); P rounded to T is the B operand of P.V
+        // online softmax (base 2); P rounded to T is the B operand of P.V.  The tile's row max is
+        // taken only on the first tile, which sets the running max m.  Past it, x = s*c - m is
+        // formed in place and p = exp2(x) taken at once: every p of a lane is at most the lane's
+        // sum, which is formed anyway.  While each lane's sum stays within SUMMAX, m stays.  Past
+        // that, the wave takes the row max from x and moves m up to it: after P.V when every sum
+        // is still within PLIMIT (P as formed is representable, and O and the sums take the factor
+        // after this tile's products), else before it, with P formed again.  A stale m costs no
+        // precision in floating point; the bounds keep P within f16's range and O far from fp32's
+        // (|O| grows to at most SUMMAX * S_k / 64 times max |V| before m moves).
+        constexpr bool HALF = std::is_same<T, F16>::value;
+        constexpr float SUMMAX = HALF ? 4096.f : 65536.f;         // 2^12, 2^16
+        constexpr float PLIMIT = HALF ? 32768.f : 4294967296.f;   // 2^15, 2^32
         u32x4 pf[QB][BC / 16];
+        float ps[QB], pr[QB], dl[QB];
+        auto exp_pack = [&](int qb) __attribute__((always_inline)) {
+            float sum = 0.f, lr = lrnd[qb];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float e[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        e[j] = __builtin_amdgcn_exp2f(s[qb][kb2][h * 8 + j]);
+                        sum += e[j];
+                    }
+                    const u32x4 pk = u32x4{pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]),
+                                           pack2<T>(e[6], e[7])};
+                    pf[qb][kb2 * 2 + h] = pk;
+                    lr = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr))));
+                }
+            ps[qb] = sum;
+            pr[qb] = lr;
+        };
+        // new running max mnew >= m for row qb; O and the sums take alpha = exp2(m - mnew)
+        auto raise_max = [&](int qb, float mnew) __attribute__((always_inline)) {
+            const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - (mnew == -INFINITY ? 0.f : mnew));
+            mrow[qb] = mnew;
+            lrow[qb] *= alpha;
+            lrnd[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+        };
+        auto row_max = [&](int qb) __attribute__((always_inline)) {
             float mx = -INFINITY;
 #pragma unroll
             for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb2][i]);
-            mx = xhalf_max(mx) * c;
-            // O and the row sums are rescaled only when some row of the wave raises its max by
-            // more than RESCALE_LOG2 (wave-uniform branch; other rows get alpha = 1)
-            if (__builtin_amdgcn_ballot_w64(mx > mrow[qb] + RESCALE_LOG2) != 0) {
-                const float mnew = fmaxf(mrow[qb], mx);
-                const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - (mnew == -INFINITY ? 0.f : mnew));
-                mrow[qb] = mnew;
-                lrow[qb] *= alpha;
-                lrnd[qb] *= alpha;
+            return xhalf_max(mx);
+        };
+        if (t == 0) {
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+            for (int qb = 0; qb < QB; ++qb) raise_max(qb, fmaxf(mrow[qb], row_max(qb) * c));
+        }
+        bool over = false, big = false;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mb = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[qb][kb2][i] = __builtin_fmaf(s[qb][kb2][i], c, -mb);
+            exp_pack(qb);
+            over |= __builtin_amdgcn_ballot_w64(!(ps[qb] <= SUMMAX)) != 0;
+            big |= __builtin_amdgcn_ballot_w64(!(ps[qb] <= PLIMIT)) != 0;
+        }
+        bool defer = false;
+        if (over) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) dl[qb] = fmaxf(row_max(qb), 0.f);   // rows without keys: 0
+            if (big) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    if (__builtin_amdgcn_ballot_w64(dl[qb] > 0.f) != 0) {
+                        raise_max(qb, mrow[qb] + dl[qb]);
+#pragma unroll
+                        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) s[qb][kb2][i] -= dl[qb];
+                        exp_pack(qb);
+                    }
+            } else {
+                defer = true;
             }
-            const float mbase = (mrow[qb] == -INFINITY) ? 0.f : mrow[qb];
+        }
+        // lrow: fp32 sum of p, for the LSE.  lrnd: sum of p rounded to T (the values P.V uses),
+        // for the normalisation of O: with a stale max the largest p of a row is not 1, and its
+        // rounding cancels only if numerator and denominator see the same value.
 #pragma unroll
-            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s[qb][kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb2][i], c, -mbase));
-            // lrow: fp32 sum of p, for the LSE.  lrnd: sum of p rounded to T (the values P.V
-            // uses), for the normalisation of O: with a stale max the largest p of a row is not
-            // 1, and its rounding cancels only if numerator and denominator see the same value.
-            float ls = lrow[qb], lr = lrnd[qb];
-#pragma unroll
-            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) ls += s[qb][kb2][i];
-            lrow[qb] = ls;
-#pragma unroll
-            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int o = h * 8;
-                    const u32x4 pk = u32x4{pack2<T>(s[qb][kb2][o + 0], s[qb][kb2][o + 1]),
-                                           pack2<T>(s[qb][kb2][o + 2], s[qb][kb2][o + 3]),
-                                           pack2<T>(s[qb][kb2][o + 4], s[qb][kb2][o + 5]),
-                                           pack2<T>(s[qb][kb2][o + 6], s[qb][kb2][o + 7])};
-                    pf[qb][kb2 * 2 + h] = pk;
-                    lr = sum2<T>(pk[0], sum2<T>(pk[1], sum2<T>(pk[2], sum2<T>(pk[3], lr))));
-                }
-            lrnd[qb] = lr;
+        for (int qb = 0; qb < QB; ++qb) {
+            lrow[qb] += ps[qb];
+            lrnd[qb] = pr[qb];
         }
         // O^T += V^T P^T; V^T is fetched with two transposing LDS reads per operand
         {
@@ -433,6 +478,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                 for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_32x32x16<T>(a, pf[qb][ks], oacc[qb][db]);
                 __builtin_amdgcn_sched_barrier(0);
             });
+        }
+        if (defer) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                if (__builtin_amdgcn_ballot_w64(dl[qb] > 0.f) != 0) raise_max(qb, mrow[qb] + dl[qb]);
         }
     };
 

@@ -157,6 +157,60 @@ def test_invariant_inputs(oracle, d, causal):
     assert float((lse.cpu().double() - ref_lse).abs().max()) <= 1e-3
 
 
+def _rising_inputs(kind, B, H, S, d, dtype, seed):
+    """Scores that grow along the keys, so the running max keeps moving: every query and key
+    share a component along u = (1, ..., 1), with a key weight r_j.  In base-2 units the score
+    is about r_j * sqrt(d) * log2(e) above the noise: 'ramp3' and 'ramp12' raise it by 3 and 12
+    per 128 keys; 'step20', 'step40' and 'step150' jump by that much at key 256 (past 2^15 a
+    probability does not fit f16, past 2^32 the kernel forms P again for bf16 too, and 2^150
+    overflows fp32, so p = exp2 of the score over a stale max is infinite there)."""
+    g = torch.Generator().manual_seed(seed)
+    j = torch.arange(S, dtype=torch.float64)
+    unit = float(np.sqrt(d) * np.log2(np.e))
+    if kind == "ramp3":
+        r = j * (3.0 / 128) / unit
+    elif kind == "ramp12":
+        r = j * (12.0 / 128) / unit
+    else:
+        r = (j >= 256).double() * (float(kind[4:]) / unit)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    q = (0.5 * torch.randn(B, H, S, d, generator=g, dtype=torch.float64) + 1.0).to(dt)
+    k = (0.5 * torch.randn(B, H, S, d, generator=g, dtype=torch.float64) + r[None, None, :, None]).to(dt)
+    v = torch.randn(B, H, S, d, generator=g, dtype=torch.float64).to(dt)
+    return q, k, v
+
+
+CLASSIC = [s for s in SCHEDULES if s[0] == 1]
+
+
+@pytest.mark.parametrize("kind", ["ramp3", "ramp12", "step20", "step40", "step150"])
+@pytest.mark.parametrize("sched", [None] + CLASSIC, ids=lambda s: "default" if s is None else "s%d_%d_%d_%d_%d" % s)
+def test_rising_scores(oracle, kind, sched):
+    """Running max raised inside the key loop, by small and by overflowing steps, on every
+    classic schedule: the row-sum bound must catch it and the update must keep O and LSE exact."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    if sched is not None:
+        ea.set_policy(*sched)
+    try:
+        for d in (64, 128):
+            if sched is not None and sched in D64_ONLY and d != 64:
+                continue
+            for dtype in ("bf16", "f16"):
+                for causal in (False, True):
+                    q, k, v = _rising_inputs(kind, 1, 2, 700, d, dtype, seed=d + 2 * causal)
+                    U.say(f"[gpu] rising {kind} sched={sched} d={d} {dtype} causal={causal}")
+                    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=d ** -0.5)
+                    torch.cuda.synchronize()
+                    ro, rl = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal,
+                                              d ** -0.5)
+                    st = U.compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, dtype)
+                    assert st["pass"], (kind, sched, d, dtype, causal, st)
+    finally:
+        ea.set_policy(ea.ATTN_SCHED_DEFAULT)
+
+
 def test_deterministic(oracle):
     w = I.random_workload(2, 4, 777, 777, 128, "bf16", True, seed=77)
     x = I.make_inputs(w)
