@@ -99,6 +99,7 @@ template <> __device__ __forceinline__ float sum2<F16>(uint32_t a, float acc) {
 // until then p = exp2(s*c - m) <= 2^RESCALE_LOG2 and the O rescale is skipped.  (The classic
 // kernel bounds the row sums instead, which it forms anyway.)
 constexpr float RESCALE_LOG2 = 8.0f;
+constexpr float RESCALE_MAX = 256.0f;   // 2^RESCALE_LOG2
 
 // Row max between lane l and lane l^32 (the two halves of a 32x32 accumulator column).
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -1303,22 +1304,15 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
                 for (int i = 0; i < 16; ++i)
                     if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[kb2][i] = -INFINITY;
         }
-        // online softmax of the biased base-2 scores raw * ct + bt
+        // online softmax of the biased base-2 scores raw * ct + bt.  As in the 16-bit kernel, the
+        // tile's row max is taken only on the first tile; past it x = raw * ct + bt - m is formed
+        // in place and p' = exp2(x) at once, and the lane's sum of p' bounds each p'.  A sum past
+        // 2^RESCALE_LOG2 (E4M3 holds p' only up to 448) moves m up to the row max, taken from x,
+        // before P.V, and P' is formed again.
         const float ct = cq * kdt;
         const float bt = __builtin_amdgcn_logf(vdt);   // log2
         const float ivd = __builtin_amdgcn_rcpf(vdt);
-        float mq[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float m0 = fmaxf(s[k][0], s[k][1]);
-#pragma unroll
-            for (int i = 2; i < 16; ++i) m0 = fmaxf(m0, s[k][i]);
-            mq[k] = m0;
-        }
-        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-        mx = __builtin_fmaf(xhalf_max(mx), ct, bt);
-        if (__builtin_amdgcn_ballot_w64(mx > mrow + RESCALE_LOG2) != 0) {
-            const float mnew = fmaxf(mrow, mx);
+        auto raise_max = [&](float mnew) __attribute__((always_inline)) {
             const float alpha = __builtin_amdgcn_exp2f(mrow - (mnew == -INFINITY ? 0.f : mnew));
             mrow = mnew;
             lrow *= alpha;
@@ -1327,27 +1321,57 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        }
-        const float off = bt - ((mrow == -INFINITY) ? 0.f : mrow);
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+        };
+        auto lane_max = [&]() __attribute__((always_inline)) {
+            float mq[4];
 #pragma unroll
-        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+            for (int k = 0; k < 4; ++k) {
+                float m0 = fmaxf(s[k][0], s[k][1]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[kb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][i], ct, off));
-                ls[i & 3] += s[kb2][i];
+                for (int i = 2; i < 16; ++i) m0 = fmaxf(m0, s[k][i]);
+                mq[k] = m0;
             }
-        lrow += ((ls[0] + ls[1]) + (ls[2] + ls[3])) * ivd;
+            return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+        };
+        if (t == 0) raise_max(fmaxf(mrow, __builtin_fmaf(xhalf_max(lane_max()), ct, bt)));
+        {
+            const float off = bt - ((mrow == -INFINITY) ? 0.f : mrow);
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb2][i] = __builtin_fmaf(s[kb2][i], ct, off);
+        }
         // P'^T in E4M3: dword w of k-step kk = keys of s[2 kk + w / 4][4 (w % 4) .. + 3]
         i32x8 pf[BC / 64];
+        auto exp_pack = [&]() __attribute__((always_inline)) {
+            float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < BC / 64; ++kk)
+            for (int kk = 0; kk < BC / 64; ++kk)
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const f32x16 &sv = s[2 * kk + (w >> 2)];
-                const int o = 4 * (w & 3);
-                pf[kk][w] = pack4_e4m3(sv[o], sv[o + 1], sv[o + 2], sv[o + 3]);
-            }
+                for (int w = 0; w < 8; ++w) {
+                    const f32x16 &sv = s[2 * kk + (w >> 2)];
+                    const int o = 4 * (w & 3);
+                    float e[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        e[j] = __builtin_amdgcn_exp2f(sv[o + j]);
+                        ls[j] += e[j];
+                    }
+                    pf[kk][w] = pack4_e4m3(e[0], e[1], e[2], e[3]);
+                }
+            return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        };
+        float lsum = exp_pack();
+        if (__builtin_amdgcn_ballot_w64(!(lsum <= RESCALE_MAX)) != 0) {
+            const float d = fmaxf(xhalf_max(lane_max()), 0.f);   // rows without keys: 0
+            raise_max(mrow + d);
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb2][i] -= d;
+            lsum = exp_pack();
+        }
+        lrow += lsum * ivd;
         // sum of the rounded p' (the weights P.V uses): ones x P'^T on the matrix core
         f32x16 rs = {};
 #pragma unroll

@@ -157,7 +157,7 @@ def test_invariant_inputs(oracle, d, causal):
     assert float((lse.cpu().double() - ref_lse).abs().max()) <= 1e-3
 
 
-def _rising_inputs(kind, B, H, S, d, dtype, seed):
+def _rising_inputs(kind, B, H, S, d, dtype, seed, knoise=0.5):
     """Scores that grow along the keys, so the running max keeps moving: every query and key
     share a component along u = (1, ..., 1), with a key weight r_j.  In base-2 units the score
     is about r_j * sqrt(d) * log2(e) above the noise: 'ramp3' and 'ramp12' raise it by 3 and 12
@@ -175,7 +175,7 @@ def _rising_inputs(kind, B, H, S, d, dtype, seed):
         r = (j >= 256).double() * (float(kind[4:]) / unit)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float16
     q = (0.5 * torch.randn(B, H, S, d, generator=g, dtype=torch.float64) + 1.0).to(dt)
-    k = (0.5 * torch.randn(B, H, S, d, generator=g, dtype=torch.float64) + r[None, None, :, None]).to(dt)
+    k = (knoise * torch.randn(B, H, S, d, generator=g, dtype=torch.float64) + r[None, None, :, None]).to(dt)
     v = torch.randn(B, H, S, d, generator=g, dtype=torch.float64).to(dt)
     return q, k, v
 
@@ -209,6 +209,32 @@ def test_rising_scores(oracle, kind, sched):
                     assert st["pass"], (kind, sched, d, dtype, causal, st)
     finally:
         ea.set_policy(ea.ATTN_SCHED_DEFAULT)
+
+
+@pytest.mark.parametrize("kind", ["ramp3", "ramp12", "step20", "step150"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_rising_scores_fp8(oracle, kind, fmt):
+    """The same rising scores through the fp8 kernel (block-quantised from the fp32 values).  The
+    keys' own noise is small here, so that a row's weight spreads over many keys: P in E4M3 has
+    4 significant bits, and a row dominated by two or three keys would test that rounding (a
+    property of the fp8 path), not the running max."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    for d in (64, 128):
+        for causal in (False, True):
+            q, k, v = (t.float().numpy() for t in _rising_inputs(kind, 1, 2, 700, d, "bf16", seed=d + 2 * causal,
+                                                                  knoise=0.05))
+            codes = [I.quantize_fp8_blocks(t, fmt) for t in (q, k, v)]
+            U.say(f"[gpu] rising fp8 {kind} {fmt} d={d} causal={causal}")
+            o, lse = ea.fwd_fp8(*(torch.from_numpy(c).to(dev) for c, _ in codes),
+                                *(torch.from_numpy(ds).to(dev) for _, ds in codes),
+                                causal=causal, scale=d ** -0.5, fmt=fmt)
+            torch.cuda.synchronize()
+            qx, kx, vx = (oracle.decode_fp8_blocks(c, ds, fmt) for c, ds in codes)
+            ro, rl = oracle.attention(qx, kx, vx, causal, d ** -0.5)
+            st = U.compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "fp8")
+            assert st["pass"], (kind, fmt, d, causal, st)
 
 
 def test_deterministic(oracle):
