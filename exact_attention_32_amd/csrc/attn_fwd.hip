@@ -187,12 +187,12 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
 
 // Direct-to-LDS loads of this wave's share of one K tile and one V tile: rows [k0, k0 + ROWS) of
 // a head, ROWB bytes per row, into LDS at kst and vst.  Block j (1 KiB) of the wave: lane l's 16
-// bytes come from row grow[j], byte column gcolb[j], i.e. byte goff[j] of a full tile.  In the
-// S_k tail, rows past S_k are clamped onto the last key: their scores are masked to -inf and their
-// P is exactly 0, so any finite value is harmless.
+// bytes come from byte goff[j] of a full tile: row goff[j] / ROWB, byte column goff[j] % ROWB.  In
+// the S_k tail, rows past S_k are clamped onto the last key: their scores are masked to -inf and
+// their P is exactly 0, so any finite value is harmless.  (The row and column are derived from
+// goff where needed, so they take no registers through the key loop.)
 template <int BPW, int ROWS, int ROWB>
 __device__ __forceinline__ void load_kv_tile(const unsigned char *kh, const unsigned char *vh, int k0, int Sk,
-                                             const int (&grow)[BPW], const int (&gcolb)[BPW],
                                              const uint32_t (&goff)[BPW], uint32_t kst, uint32_t vst, int wave) {
     const unsigned char *kt = kh + (size_t)k0 * ROWB, *vt = vh + (size_t)k0 * ROWB;
     if (k0 + ROWS <= Sk) {
@@ -205,7 +205,8 @@ __device__ __forceinline__ void load_kv_tile(const unsigned char *kh, const unsi
     } else {
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
-            const uint32_t o = (uint32_t)((min(k0 + grow[j], Sk - 1) - k0) * ROWB + gcolb[j]);
+            const int row = (int)(goff[j] / ROWB), colb = (int)(goff[j] % ROWB);
+            const uint32_t o = (uint32_t)((min(k0 + row, Sk - 1) - k0) * ROWB + colb);
             const uint32_t off = (uint32_t)((wave * BPW + j) * 1024);
             dma16s(kt, o, kst + off);
             dma16s(vt, o, vst + off);
@@ -311,8 +312,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const uint32_t smem0 = lds_addr(&smem[0][0][0]);
     auto dma = [&](int t) __attribute__((always_inline)) {
         const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
-        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, t * BC, Sk, grow, gcolb,
-                                    goff, st, st + TILEB, wave);
+        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, t * BC, Sk, goff, st,
+                                    st + TILEB, wave);
     };
 
     const float c = p.c;
@@ -626,8 +627,8 @@ __global__ __launch_bounds__(512) void attn_fwd_dp_kernel(Params p) {
     const uint32_t smem0 = lds_addr(&smem[0][0][0]);
     auto dma = [&](int t) __attribute__((always_inline)) {
         const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
-        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, t * BC, Sk, grow, gcolb,
-                                    goff, st, st + TILEB, wave);
+        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, t * BC, Sk, goff, st,
+                                    st + TILEB, wave);
     };
 
     u32x4 qf[D / 16];
@@ -852,8 +853,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
 
     auto dma = [&](int t) __attribute__((always_inline)) {
         const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
-        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, t * BC, Sk, grow, gcolb,
-                                    goff, st, st + TILEB, wave);
+        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, t * BC, Sk, goff, st,
+                                    st + TILEB, wave);
     };
 
     // V(t) -> V^T(t): the (dv block, k-step) chunks are split over the 8 waves; each call does
@@ -1239,7 +1240,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
     const uint32_t smem0 = lds_addr(&smem[0][0][0]);
     auto dma = [&](int t) __attribute__((always_inline)) {
         const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
-        load_kv_tile<BPW, BC, ROWB>(Kh, Vh, t * BC, Sk, grow, gcolb, goff, st, st + TILEB, wave);
+        load_kv_tile<BPW, BC, ROWB>(Kh, Vh, t * BC, Sk, goff, st, st + TILEB, wave);
     };
 
     i32x8 qf[KSTEPS];
