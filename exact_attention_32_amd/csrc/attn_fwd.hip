@@ -205,7 +205,9 @@ __device__ __forceinline__ void load_kv_tile(const unsigned char *kh, const unsi
     } else {
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
-            const int row = (int)(goff[j] / ROWB), colb = (int)(goff[j] % ROWB);
+            uint32_t g = goff[j];
+            asm volatile("" : "+v"(g));   // derived here, not hoisted out of the key loop
+            const int row = (int)(g / ROWB), colb = (int)(g % ROWB);
             const uint32_t o = (uint32_t)((min(k0 + row, Sk - 1) - k0) * ROWB + colb);
             const uint32_t off = (uint32_t)((wave * BPW + j) * 1024);
             dma16s(kt, o, kst + off);
