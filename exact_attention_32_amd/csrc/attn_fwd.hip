@@ -99,7 +99,6 @@ template <> __device__ __forceinline__ float sum2<F16>(uint32_t a, float acc) {
 // until then p = exp2(s*c - m) <= 2^RESCALE_LOG2 and the O rescale is skipped.  (The classic
 // kernel bounds the row sums instead, which it forms anyway.)
 constexpr float RESCALE_LOG2 = 8.0f;
-constexpr float RESCALE_MAX = 256.0f;   // 2^RESCALE_LOG2
 
 // Row max between lane l and lane l^32 (the two halves of a 32x32 accumulator column).
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -1108,16 +1107,25 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
 //
 // Q, K, V hold OCP fp8 codes, all three E4M3 or all three E5M2 (the template argument FMT; the
 // deep dive's section 4 names both formats); the value of row r of a head is
-// code * descale[r / 128].  One key
-// tile is one descale block (128 keys).  With raw = Q_code . K_code (exact in the fp32 MFMA
-// accumulator), the base-2 score is raw * c_t with c_t = scale * log2(e) * qd * kd_t.  V's
-// descale enters as a per-tile bias of the exponent: the kernel keeps the running max m of
-// raw * c_t + log2(vd_t) and forms p' = exp2(raw * c_t + log2(vd_t) - m) = vd_t * p, so that
-// sum_j p'_j * Vcode_j = sum_j p_j * V_j with no per-tile rescale of O; the row sums take p'
-// times 1 / vd_t.  p' <= 2^RESCALE_LOG2 = 256 fits E4M3 (largest finite 448), and P' is rounded
-// to E4M3 for either input format: the matrix core takes a different format for each operand,
-// and E4M3 keeps one more mantissa bit of the probabilities than E5M2 would.
+// code * descale[r / 128].  One key tile is one descale block (128 keys).  With raw = Q_code . K_code
+// (exact in the fp32 MFMA accumulator), the base-2 score is x = raw * c_t with
+// c_t = scale * log2(e) * qd * kd_t.
 //
+// P' for the P.V product is rounded to E4M3 (for either input format: the matrix core takes a
+// format per operand, and E4M3 keeps one more mantissa bit of the probabilities than E5M2).  Its
+// range is kept away from both ends of E4M3:
+//   * headroom: the running offset m is set to a row's max minus 8, so the largest P' of the tile
+//     that sets it is 2^8 = 256 and keys 17 binades below it are still representable (E4M3's
+//     smallest subnormal is 2^-9).  m moves only when a later tile's P' would pass 2^8.75 (E4M3's
+//     largest finite value is 448 = 2^8.81): the tile's lane max of the exponents is checked every
+//     tile, and a raise puts that tile's max back at 2^8.
+//   * V's descale never shifts P': vd_t = f_t * 2^e_t with f_t in [0.5, 1).  2^e_t is the E8M0
+//     block scale of the V^T operand of the scaled MFMA (the matrix core applies it exactly), and
+//     only log2(f_t), in [-1, 0), enters the exponent of P'.  So P' = exp2(x + log2 f_t - m), the
+//     weights P.V applies are round(P') / f_t, and the row sums add (sum P') / f_t per tile.
+//     (A descale below 2^-126 is taken as 2^-126 with f_t = 1: such a block's V values are below
+//     448 * 2^-126 in magnitude, so the difference is below 6e-36.)
+
 // MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales; operand format 0 = E4M3,
 // 1 = E5M2).  It sums A[i][k] B[k][j] over
 // the pairs (lane half, byte) that A and B share, so any key order that both operands use is
@@ -1147,6 +1155,16 @@ template <int FA, int FB>
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
 }
+// the same with A scaled by 2^(sa - 127) (sa: an E8M0 exponent byte, 0..254, uniform over the wave)
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mfma_f8_sa(const i32x8 &a, const i32x8 &b, const f32x16 &c, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, 127);
+}
+
+// P' headroom: the tile that sets the running offset m puts its largest P' at 2^P8_HEAD; m moves
+// again only when a P' would pass 2^P8_LIMIT (448 = 2^8.807 is E4M3's largest finite value)
+constexpr float P8_HEAD = 8.0f;
+constexpr float P8_LIMIT = 8.75f;
 
 // four floats -> four E4M3 bytes (round to nearest even), first value in the low byte.  The
 // first conversion's "old" operand only supplies bytes 2-3, which the second one overwrites, so
@@ -1307,14 +1325,28 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
                 for (int i = 0; i < 16; ++i)
                     if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[kb2][i] = -INFINITY;
         }
-        // online softmax of the biased base-2 scores raw * ct + bt.  As in the 16-bit kernel, the
-        // tile's row max is taken only on the first tile; past it x = raw * ct + bt - m is formed
-        // in place and p' = exp2(x) at once, and the lane's sum of p' bounds each p'.  A sum past
-        // 2^RESCALE_LOG2 (E4M3 holds p' only up to 448) moves m up to the row max, taken from x,
-        // before P.V, and P' is formed again.
+        // V's descale: vd_t = vf * 2^(vsc - 127) with vf in [0.5, 1) (see the header above)
+        const uint32_t vbits = __float_as_uint(vdt);
+        const int vexp = (int)((vbits >> 23) & 0xff);
+        int vsc;
+        float vf;
+        if (vexp == 0) {
+            vsc = 1;
+            vf = 1.f;
+        } else if (vexp >= 254) {
+            vsc = 254;
+            vf = __uint_as_float((vbits & 0x807fffffu) | (127u << 23));
+        } else {
+            vsc = vexp + 1;
+            vf = __uint_as_float((vbits & 0x807fffffu) | (126u << 23));
+        }
+        // online softmax of the base-2 exponents y = raw * ct + log2(vf).  The first tile sets the
+        // running offset m = (row max of y) - P8_HEAD.  Later tiles form x = y - m in place and
+        // p' = exp2(x) at once; the lane max of x is checked against P8_LIMIT, and only a wave
+        // where some lane passes it moves m (x's row max back to P8_HEAD) and forms P' again.
         const float ct = cq * kdt;
-        const float bt = __builtin_amdgcn_logf(vdt);   // log2
-        const float ivd = __builtin_amdgcn_rcpf(vdt);
+        const float lvf = __builtin_amdgcn_logf(vf);   // log2(vf), in [-1, 0]
+        const float ivf = __builtin_amdgcn_rcpf(vf);
         auto raise_max = [&](float mnew) __attribute__((always_inline)) {
             const float alpha = __builtin_amdgcn_exp2f(mrow - (mnew == -INFINITY ? 0.f : mnew));
             mrow = mnew;
@@ -1336,14 +1368,15 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             }
             return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
         };
-        if (t == 0) raise_max(fmaxf(mrow, __builtin_fmaf(xhalf_max(lane_max()), ct, bt)));
+        if (t == 0) raise_max(fmaxf(mrow, __builtin_fmaf(xhalf_max(lane_max()), ct, lvf) - P8_HEAD));
         {
-            const float off = bt - ((mrow == -INFINITY) ? 0.f : mrow);
+            const float off = lvf - ((mrow == -INFINITY) ? 0.f : mrow);
 #pragma unroll
             for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[kb2][i] = __builtin_fmaf(s[kb2][i], ct, off);
         }
+        const float xmax = (t == 0) ? 0.f : lane_max();
         // P'^T in E4M3: dword w of k-step kk = keys of s[2 kk + w / 4][4 (w % 4) .. + 3]
         i32x8 pf[BC / 64];
         auto exp_pack = [&]() __attribute__((always_inline)) {
@@ -1365,8 +1398,9 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             return (ls[0] + ls[1]) + (ls[2] + ls[3]);
         };
         float lsum = exp_pack();
-        if (__builtin_amdgcn_ballot_w64(!(lsum <= RESCALE_MAX)) != 0) {
-            const float d = fmaxf(xhalf_max(lane_max()), 0.f);   // rows without keys: 0
+        if (__builtin_amdgcn_ballot_w64(xmax > P8_LIMIT) != 0) {
+            const float rm = xhalf_max(xmax);
+            const float d = rm > P8_LIMIT ? rm - P8_HEAD : 0.f;
             raise_max(mrow + d);
 #pragma unroll
             for (int kb2 = 0; kb2 < BC / 32; ++kb2)
@@ -1374,7 +1408,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
                 for (int i = 0; i < 16; ++i) s[kb2][i] -= d;
             lsum = exp_pack();
         }
-        lrow += lsum * ivd;
+        lrow += lsum * ivf;
         // sum of the rounded p' (the weights P.V uses): ones x P'^T on the matrix core
         f32x16 rs = {};
 #pragma unroll
@@ -1397,10 +1431,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             constexpr int j = decltype(J)::value, kk = j / (D / 32), db = j % (D / 32);
             const i32x8 a = ring[j % PV_AHEAD];
             if constexpr (j + PV_AHEAD < NPV) ring[j % PV_AHEAD] = pv_fetch(std::integral_constant<int, j + PV_AHEAD>{});
-            oacc[db] = mfma_f8<FMT, 0>(a, pf[kk], oacc[db]);
+            oacc[db] = mfma_f8_sa<FMT, 0>(a, pf[kk], oacc[db], vsc);
             __builtin_amdgcn_sched_barrier(0);
         });
-        lrnd += rs[0] * ivd;
+        lrnd += rs[0] * ivf;
     };
 
     constexpr int LPT = 2 * BPW;

@@ -46,25 +46,49 @@ def rounding_floor(o_ref: np.ndarray, dtype: str) -> np.ndarray:
     return np.abs(t - o_ref)
 
 
+def ulp_distance(a: np.ndarray, b: np.ndarray, dtype: str) -> np.ndarray:
+    """Distance in units in the last place between two arrays of values representable in the output
+    type (bf16 or f16), counted along the ordered bit patterns (a step across a binade boundary is
+    one ulp; +0 and -0 are the same point)."""
+    dt = _OUT_DT[dtype]
+    ia = torch.from_numpy(np.ascontiguousarray(a)).to(dt).view(torch.int16).numpy().astype(np.int64)
+    ib = torch.from_numpy(np.ascontiguousarray(b)).to(dt).view(torch.int16).numpy().astype(np.int64)
+    # sign-magnitude -> ordered integers
+    oa = np.where(ia < 0, -(ia & 0x7FFF), ia)
+    ob = np.where(ib < 0, -(ib & 0x7FFF), ib)
+    return np.abs(oa - ob)
+
+
 def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray, dtype: str):
     """Error statistics and the pass decision.
 
-    Gate: every element |O - O_ref| <= tol + |round(O_ref) - O_ref| (the stated
-    tolerance on top of the output's own rounding), and max |LSE - LSE_ref| <= 1e-3.
+    Gate, per element of O: |O - O_ref| <= tol (1e-2 for f16/bf16, 5e-2 for fp8), or else O is
+    within one ulp of the correctly rounded value RN(O_ref).  The second case is counted, in two
+    classes: RN(O_ref) itself misses tol (bf16 spacing is 2^-6 in [2, 4) and 2^-5 in [4, 8), so no
+    output of the type meets tol there), or RN(O_ref) meets tol and O is its neighbour.
+    LSE: max |LSE - LSE_ref| <= 1e-3.  The raw max |O - O_ref| and the rounding floor are reported.
     """
+    tol = TOL_O[dtype]
     err = np.abs(o_gpu - o_ref)
     floor = rounding_floor(o_ref, dtype)
-    excess = err - floor
     lerr = np.abs(lse_gpu - lse_ref)
+    over = err > tol
+    rounded = torch.from_numpy(np.ascontiguousarray(o_ref)).to(_OUT_DT[dtype]).double().numpy()
+    one_ulp = over & (ulp_distance(o_gpu, rounded, dtype) <= 1)
+    failed = over & ~one_ulp
     stats = {
-        "max_abs_err_O": float(err.max()),
-        "rms_err_O": float(np.sqrt(np.mean(err ** 2))),
-        "floor_O": float(floor.max()),
-        "max_err_over_floor_O": float(excess.max()),
-        "max_abs_err_LSE": float(lerr.max()),
+        "max_abs_err_O": float(err.max()) if err.size else 0.0,
+        "rms_err_O": float(np.sqrt(np.mean(err ** 2))) if err.size else 0.0,
+        "floor_O": float(floor.max()) if floor.size else 0.0,
+        "n_elements": int(err.size),
+        "n_over_tol": int(over.sum()),
+        "n_one_ulp_rn_misses_tol": int((one_ulp & (floor > tol)).sum()),
+        "n_one_ulp_neighbour": int((one_ulp & (floor <= tol)).sum()),
+        "n_failed": int(failed.sum()),
+        "max_abs_err_LSE": float(lerr.max()) if lerr.size else 0.0,
         "finite": bool(np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))),
     }
-    stats["pass"] = bool(stats["finite"] and excess.max() <= TOL_O[dtype] and lerr.max() <= TOL_LSE)
+    stats["pass"] = bool(stats["finite"] and stats["n_failed"] == 0 and stats["max_abs_err_LSE"] <= TOL_LSE)
     return stats
 
 

@@ -1,9 +1,9 @@
 """GPU parity: the HIP kernels against the fp64 oracle, element by element.
 
-Gate: max |O - O_ref| <= 1e-2 for f16/bf16 and 5e-2 for fp8 (E4M3 and E5M2),
-measured on top of each element's own output rounding
-(|round(O_ref) - O_ref|, which alone can exceed 1e-2 where |O| >= 4 in bf16);
-max |LSE - LSE_ref| <= 1e-3.
+Gate, per element: |O - O_ref| <= 1e-2 for f16/bf16 and 5e-2 for fp8 (E4M3 and E5M2), or else O
+within one ulp of the correctly rounded RN(O_ref) (bf16 spacing is 2^-6 in [2, 4) and 2^-5 in
+[4, 8), so there a correctly rounded output alone can miss 1e-2); such elements are counted and
+reported, split by whether RN(O_ref) itself misses the tolerance; max |LSE - LSE_ref| <= 1e-3.
 """
 import numpy as np
 import pytest
@@ -151,10 +151,9 @@ def test_invariant_inputs(oracle, d, causal):
     n = torch.arange(1, S + 1, dtype=torch.float64)
     ref = (vv.cumsum(2) / n[None, None, :, None]) if causal else vv.mean(2, keepdim=True).expand_as(vv)
     ref_lse = torch.log(n) if causal else torch.full((S,), float(np.log(S)), dtype=torch.float64)
-    err = (o.cpu().double() - ref).abs()
-    floor = torch.from_numpy(U.rounding_floor(ref.numpy(), "bf16"))
-    assert float((err - floor).max()) <= 1e-2
-    assert float((lse.cpu().double() - ref_lse).abs().max()) <= 1e-3
+    st = U.compare(o.cpu().double().numpy(), lse.cpu().double().numpy(), ref.numpy(),
+                   ref_lse[None, None, :].expand(B, H, S).numpy(), "bf16")
+    assert st["pass"], st
 
 
 def _rising_inputs(kind, B, H, S, d, dtype, seed, knoise=0.5):
@@ -247,24 +246,20 @@ def test_deterministic(oracle):
 
 
 @pytest.mark.parametrize("name", sorted(I.WORKLOADS))
-def test_workload_sampled_rows(oracle, name):
-    """Full-size workloads in the benchmark's launch configuration, checked on sampled rows."""
+def test_workload_full(oracle, name):
+    """Every full-size workload in the benchmark's launch configuration, every element of O and LSE
+    against the oracle (the fp64 oracle takes a few seconds per workload on the host's cores)."""
     w = I.WORKLOADS[name]
     x = I.make_inputs(w)
-    U.say(f"[gpu] {name}")
+    U.say(f"[gpu] full {name}")
     o, lse = U.run_gpu(x)
-    o = o.view(w.B * w.H, w.S_q, w.d)
-    lse = lse.view(w.B * w.H, w.S_q)
-    rows = U.sample_rows(w, n_random=200, seed=w.seed)
-    og = o[rows[:, 0], rows[:, 1]].double().cpu().numpy()
-    lg = lse[rows[:, 0], rows[:, 1]].double().cpu().numpy()
+    og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    del o, lse
     q, k, v = U.oracle_inputs(x, oracle)
-    ro, rl = oracle.attention_rows(q, k, v, w.causal, w.scale, rows)
+    ro, rl = oracle.attention(q, k, v, w.causal, w.scale)
     st = U.compare(og, lg, ro, rl, w.dtype)
-    U.say(f"   {st}")
+    U.say(f"   {name}: {st}")
     assert st["pass"], st
-    # properties at every row: finite outputs; LSE of a causal row i is >= log-free bound: LSE >= s_ii
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
 @pytest.mark.parametrize("name", ["fp8_b2_h16_s4096_d128", "e5m2_b2_h16_s4096_d128"])
@@ -383,3 +378,64 @@ def test_graph_replay_equals_eager(oracle, dtype):
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {rep} differs from the eager result"
         del junk
+
+
+def _fp8_range_inputs(kind, S, d, seed):
+    """fp32 Q, K, V [1, 1, S, d] whose fp8 probabilities or V descales reach the ends of their range:
+    'sink0' / 'sinkmid': key 0 (or key S/2) eleven binades above S-1 keys of nearly equal score, V
+    N(0,1); 'sink_vsmall': the same sink at key 0 with the other V blocks scaled by 2^-10..2^-8 (V
+    descales spread over ten binades, the largest first); 'vspread0' / 'vspreadmid': V blocks scaled
+    by 2^-10..2^10 (the largest first, or in the middle), N(0,1) queries and keys."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    scale = d ** -0.5
+    nb = (S + 127) // 128
+    u = np.ones(d) / np.sqrt(d)
+    if kind.startswith("sink"):
+        q = np.tile(4.0 * u, (S, 1))
+        k = 1e-3 * rng.standard_normal((S, d))
+        j = S // 2 + 5 if kind == "sinkmid" else 0
+        k[j] += u * (11.0 / (scale * 4.0 * np.log2(np.e)))
+        v = rng.standard_normal((S, d))
+        if kind == "sink_vsmall":
+            for b in range(1, nb):
+                v[128 * b:128 * (b + 1)] *= 2.0 ** rng.uniform(-10.0, -8.0)
+    else:
+        q = rng.standard_normal((S, d))
+        k = rng.standard_normal((S, d))
+        v = rng.standard_normal((S, d))
+        ex = rng.uniform(-10.0, 10.0, nb)
+        ex[0 if kind == "vspread0" else nb // 2] = 10.0
+        for b in range(nb):
+            v[128 * b:128 * (b + 1)] *= 2.0 ** ex[b]
+    return tuple(a.astype(np.float32)[None, None] for a in (q, k, v))
+
+
+@pytest.mark.parametrize("kind", ["sink0", "sinkmid", "sink_vsmall", "vspread0", "vspreadmid"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_range(oracle, kind, fmt):
+    """The fp8 path where its probabilities span many binades (an attention sink over 4K flat keys)
+    and where V's block descales differ by up to 2^20.  The sink cases keep V at N(0,1) and are gated
+    at 5e-2.  Where V itself reaches 2^10 in magnitude, an E4M3 probability's own rounding (up to
+    2^-4 of its value) moves O by far more than 5e-2 in absolute terms, so those cases are gated at
+    5e-2 relative to the largest |O|; the descale must not shift the probabilities out of E4M3's
+    range either way."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    S = 4200
+    for d in (64, 128):
+        for causal in (False, True):
+            q, k, v = _fp8_range_inputs(kind, S, d, seed=d + 3 * causal)
+            codes = [I.quantize_fp8_blocks(t, fmt) for t in (q, k, v)]
+            U.say(f"[gpu] fp8 range {kind} {fmt} d={d} causal={causal}")
+            o, lse = ea.fwd_fp8(*(torch.from_numpy(c).to(dev) for c, _ in codes),
+                                *(torch.from_numpy(ds).to(dev) for _, ds in codes),
+                                causal=causal, scale=d ** -0.5, fmt=fmt)
+            torch.cuda.synchronize()
+            qx, kx, vx = (oracle.decode_fp8_blocks(c, ds, fmt) for c, ds in codes)
+            ro, rl = oracle.attention(qx, kx, vx, causal, d ** -0.5)
+            og, lg = o.double().cpu().numpy(), lse.double().cpu().numpy()
+            err_o, err_l = float(np.abs(og - ro).max()), float(np.abs(lg - rl).max())
+            gate = 5e-2 * (max(1.0, float(np.abs(ro).max())) if kind.startswith("vspread") else 1.0)
+            U.say(f"   max|dO| {err_o:.3e} (gate {gate:.3e}, max|O| {np.abs(ro).max():.3e}), max|dLSE| {err_l:.3e}")
+            assert np.all(np.isfinite(og)) and err_o <= gate and err_l <= U.TOL_LSE, (kind, fmt, d, causal)
