@@ -28,9 +28,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "bf16_b2_h16_s4096_d128"
-# Under back-to-back launches MI355X raises its clock over the first 30-50 ms (measured on the
-# default workload: 299 us per launch over the first 20 launches, 265 us around launch 50, 255 us
-# from launch 120 on).  The default warmup runs until that has passed.
+# Under back-to-back launches MI355X raises its engine clock over the first 30-50 ms (measured on
+# the default workload: 299 us per launch over the first 20 launches, 265 us around launch 50,
+# 255 us from launch 120 on).  Before the warmup steps, the same launch runs for CLOCK_SETTLE_S so
+# that the timed steps see the clock a sustained workload runs at; the line reports it.
+CLOCK_SETTLE_S = 0.25
 WARMUP_SECONDS = 0.25
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "e5m2": 5000.0}
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_32_amd", "csrc", "attn_fwd.hip")
@@ -69,6 +71,21 @@ def counter_traffic(kernel: str, workload: str):
         return None
 
 
+def settle_clock(step, seconds: float) -> int:
+    """Back-to-back launches of the step for `seconds` (the engine clock's ramp); returns the count."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while seconds > 0:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return n
+
+
 def warm_up(step, warmup: int) -> int:
     """Run the untimed warmup steps and return how many ran: exactly `warmup`, or for warmup < 0
     (the default) batches of 10 until WARMUP_SECONDS have passed."""
@@ -89,7 +106,7 @@ def warm_up(step, warmup: int) -> int:
             return n
 
 
-def run_gpu(work, x, steps: int, warmup: int):
+def run_gpu(work, x, steps: int, warmup: int, settle_s: float):
     import torch
 
     import exact_attention_32_amd as ea
@@ -110,6 +127,7 @@ def run_gpu(work, x, steps: int, warmup: int):
         def step():
             ea.fwd(q, k, v, causal=work.causal, scale=work.scale, out=o, lse=lse)
 
+    settled = settle_clock(step, settle_s)
     warmed = warm_up(step, warmup)
     stream = torch.cuda.current_stream(dev)   # the stream the kernel is launched on
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -123,7 +141,7 @@ def run_gpu(work, x, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, per_launch_ms, warmed
+    return wall, per_launch_ms, warmed, settled
 
 
 def main(argv=None):
@@ -133,10 +151,17 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=-1,
                     help="untimed warmup steps; default: until %.2f s have passed (the clock ramp)" % WARMUP_SECONDS)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--clock-settle", type=float, default=CLOCK_SETTLE_S, metavar="SECONDS",
+                    help="back-to-back launches before the warmup steps, so the timed steps run at the "
+                         "sustained engine clock (0: none); default %(default)s")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the attention benchmark, time the bf16 matrix-core calibration kernel "
+                         "(back-to-back 32x32x16 MFMAs on random N(0,1) operands from LDS, two waves per SIMD): "
+                         "the dense rate the chip sustains under its power limit")
     ap.add_argument("--quantize", action="store_true",
                     help="instead of the attention benchmark, time the per-block E4M3 quantiser on the fp32 Q, K, V "
                          "of the fp8 workload (HBM-bound; reports GB/s)")
@@ -156,6 +181,8 @@ def main(argv=None):
 
     if args.copy_calibration > 0:
         return copy_calibration(args.copy_calibration, max(1, args.steps))
+    if args.mfma_ceiling:
+        return bench_mfma_ceiling(args.steps, args.warmup, args.clock_settle)
     if args.quantize:
         return bench_quantize(args.steps, args.warmup, not args.no_cpu_baseline)
     if args.qknorm:
@@ -171,7 +198,7 @@ def main(argv=None):
     work = I.WORKLOADS[args.workload]
     x = I.make_inputs(work)
 
-    wall, per_launch, warmed = run_gpu(work, x, args.steps, args.warmup)
+    wall, per_launch, warmed, settled = run_gpu(work, x, args.steps, args.warmup, args.clock_settle)
     flops = work.flops()
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -195,6 +222,9 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": work.dtype,
+        "clock_settle": {"seconds": args.clock_settle, "launches": settled,
+                         "why": "MI355X ramps its engine clock over the first ~50 ms of sustained launches; "
+                                "these untimed launches precede the warmup steps"},
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": work.name, "B": work.B, "H": work.H, "S_q": work.S_q, "S_k": work.S_k, "d": work.d,
                    "causal": work.causal, "dtype": work.dtype, "scale": work.scale},
@@ -231,6 +261,65 @@ def copy_calibration(mib: int, reps: int) -> int:
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
                       "launches": reps}), flush=True)
+    return 0
+
+
+def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float) -> int:
+    """One step = one launch of the matrix-core calibration kernel on every CU."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from exact_attention_32_amd import build as B
+
+    if not os.path.exists(B.RATE_LIB):
+        raise RuntimeError(f"calibration library not built: {B.RATE_LIB}")
+    L = ctypes.CDLL(B.RATE_LIB)
+    L.attn_mfma_rate.restype = ctypes.c_int
+    L.attn_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator().manual_seed(11)
+    table = torch.randn(32768, generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    iters = 2000
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        rc = L.attn_mfma_rate(table.data_ptr(), cus, iters, out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"attn_mfma_rate: {rc}")
+
+    settled = settle_clock(step, settle_s)
+    warmed = warm_up(step, warmup)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    flops = cus * 8 * 16 * iters * 32 * 32 * 16 * 2
+    avg = float(np.mean(per))
+    result = {
+        "metric": "dense bf16 MFMA rate on random operands (matrix-core calibration)",
+        "value": round(flops / (wall / steps) / 1e12, 1), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmed, "ms_per_step": round(wall * 1e3 / steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "clock_settle": {"seconds": settle_s, "launches": settled},
+        "config": {"workload": "mfma_32x32x16_bf16_random_lds_operands", "cus": cus, "waves_per_simd": 2,
+                   "mfmas_per_wave": 16 * iters},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / 2500.0, 4), "traffic": None,
+                     "kernel": "mfma_rate_kernel", "avg_launch_us": round(avg * 1e3, 2),
+                     "algorithmic_flop_per_launch": flops},
+    }
+    print(json.dumps(result), flush=True)
     return 0
 
 
@@ -378,7 +467,7 @@ def run_cpu_baseline(work, x, target_s: float):
     from oracle import attn_oracle
 
     orc = attn_oracle.get()
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads, cpus = cpu_share()
     BH = work.B * work.H
 
     qa, ka, va = _oracle_arrays(work, x, orc)
@@ -397,8 +486,24 @@ def run_cpu_baseline(work, x, target_s: float):
     flops = work.flops() * n // BH
     used = orc.last_threads
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "host_cpus": cpus,
             "sample": f"{n} of {BH} (b,h) heads of {work.name}, all {work.S_q} query rows each, fp64 explicit "
-                      f"softmax; {t:.2f} s on {used} threads"}
+                      f"softmax; {t:.2f} s on {used} threads (host: {cpus['nproc']} CPUs, "
+                      f"{cpus['affinity']} in this process's affinity set, CPU share {cpus['share']})"}
+
+
+def cpu_share():
+    """Threads for the oracle baseline: every CPU of this process's affinity set, or the host's CPU
+    share for this GPU where the environment states one (OMP_NUM_THREADS), whichever is smaller;
+    and the counts behind that choice."""
+    affinity = len(os.sched_getaffinity(0))
+    nproc = os.cpu_count() or affinity
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    threads = min(affinity, share) if share > 0 else affinity
+    return max(1, threads), {"nproc": nproc, "affinity": affinity, "share": share if share > 0 else None}
 
 
 def _oracle_arrays(work, x, orc):

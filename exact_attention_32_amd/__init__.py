@@ -117,6 +117,21 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _check_buffer(t, name: str, shape, dtype, device):
+    """A caller-supplied output must be exactly what the kernel writes: its shape, type, device and
+    a dense layout (the library writes through the raw pointer)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: float | None = None,
         out: torch.Tensor | None = None, lse: torch.Tensor | None = None, want_lse: bool = True):
     """Exact attention forward for tensors [B, H, S, d] -> (O, LSE).
@@ -134,11 +149,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         raise ValueError(f"unsupported dtype {q.dtype}")
     if scale is None:
         scale = d ** -0.5
+    out_dt = torch.bfloat16 if dt in (ATTN_FP8_E4M3, ATTN_FP8_E5M2) else q.dtype
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16 if dt in (ATTN_FP8_E4M3, ATTN_FP8_E5M2) else q.dtype,
-                          device=q.device)
+        out = torch.empty(q.shape, dtype=out_dt, device=q.device)
+    _check_buffer(out, "out", (B, H, S_q, d), out_dt, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_buffer(lse, "lse", (B, H, S_q), torch.float32, q.device)
     rc = load_library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  lse.data_ptr() if lse is not None else None, B, H, S_q, S_k, d,
                                  int(bool(causal)), float(scale), dt, _stream(q.device))
@@ -163,15 +181,17 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scal
     for t in (q, k, v):
         if t.dtype not in (torch.uint8, _FP8_TORCH[fmt]):
             raise ValueError(f"fp8 inputs must be uint8 codes or {_FP8_TORCH[fmt]}")
-    for t, s in ((q_descale, S_q), (k_descale, S_k), (v_descale, S_k)):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (B, H, (s + 127) // 128):
-            raise ValueError("descales must be contiguous fp32 device tensors [B, H, ceil(S/128)]")
+    for t, n, s in ((q_descale, "q_descale", S_q), (k_descale, "k_descale", S_k), (v_descale, "v_descale", S_k)):
+        _check_buffer(t, n, (B, H, (s + 127) // 128), torch.float32, q.device)
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty((B, H, S_q, d), dtype=torch.bfloat16, device=q.device)
+    _check_buffer(out, "out", (B, H, S_q, d), torch.bfloat16, q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_buffer(lse, "lse", (B, H, S_q), torch.float32, q.device)
     L = load_library()
     entry = L.attn_fwd_fp8 if fmt == "e4m3" else L.attn_fwd_fp8_e5m2
     rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
@@ -200,10 +220,8 @@ def quantize_fp8(x: torch.Tensor, fmt: str = "e4m3", codes: torch.Tensor | None 
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if descale is None:
         descale = torch.empty((B, H, (S + 127) // 128), dtype=torch.float32, device=x.device)
-    if codes.shape != x.shape or codes.dtype != torch.uint8 or not codes.is_contiguous():
-        raise ValueError("codes must be a contiguous uint8 tensor of x's shape")
-    if tuple(descale.shape) != (B, H, (S + 127) // 128) or descale.dtype != torch.float32 or not descale.is_contiguous():
-        raise ValueError("descale must be a contiguous fp32 tensor [B, H, ceil(S/128)]")
+    _check_buffer(codes, "codes", tuple(x.shape), torch.uint8, x.device)
+    _check_buffer(descale, "descale", (B, H, (S + 127) // 128), torch.float32, x.device)
     L = load_library()
     entry = L.attn_quantize_e4m3 if fmt == "e4m3" else L.attn_quantize_e5m2
     rc = entry(x.data_ptr(), dt, codes.data_ptr(), descale.data_ptr(), B, H, S, d, _stream(x.device))

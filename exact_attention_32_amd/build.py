@@ -9,6 +9,9 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
 SOURCES = [SRC, os.path.join(PKG, "csrc", "quantize.hip"), os.path.join(PKG, "csrc", "qknorm.hip")]
 LIB = os.path.join(PKG, "libattn_fwd.so")
+# the matrix-core rate calibration kernel (bench.py --mfma-ceiling), a library of its own
+RATE_SRC = os.path.join(PKG, "csrc", "mfma_rate.hip")
+RATE_LIB = os.path.join(PKG, "libmfma_rate.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -28,6 +31,9 @@ def build(out: str = LIB, extra: list[str] | None = None) -> str:
     cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *(extra or []), *SOURCES, "-o", out + ".tmp"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
+    if out == LIB:
+        subprocess.run([hipcc, *HIPCC_FLAGS, RATE_SRC, "-o", RATE_LIB + ".tmp"], check=True)
+        os.replace(RATE_LIB + ".tmp", RATE_LIB)
     return out
 
 

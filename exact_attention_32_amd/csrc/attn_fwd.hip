@@ -44,6 +44,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "attn.h"
@@ -110,6 +111,13 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroups are dispatched round-robin over the XCDs (workgroup b to XCD b % nx).  With num_wg a
+// multiple of nx, work item L = (b % nx) * (num_wg / nx) + b / nx gives each XCD a contiguous range
+// of items, so all query tiles of one (b, h) share one XCD's L2 (they read the same K and V).
+__device__ __forceinline__ int xcd_order(int b, int num_wg, int nx) {
+    return (b % nx) * (num_wg / nx) + b / nx;
+}
+
 struct Params {
     const uint16_t *q, *k, *v;
     uint16_t *o;
@@ -117,7 +125,7 @@ struct Params {
     int Sq, Sk;
     int nqt;         // query tiles per (b, h)
     int num_wg;      // total workgroups
-    int xcd_remap;   // 1: map workgroups so each XCD gets a contiguous range of heads
+    int xcd_remap;   // XCD count nx: map workgroups so each XCD gets a contiguous range of heads; 0: off
     float c;         // scale * log2(e)
 };
 
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const int g = lane >> 5, l32 = lane & 31;
 
     int L = blockIdx.x;
-    if (p.xcd_remap) L = (blockIdx.x & 7) * (p.num_wg >> 3) + (blockIdx.x >> 3);
+    if (p.xcd_remap) L = xcd_order(blockIdx.x, p.num_wg, p.xcd_remap);
     const int bh = L / p.nqt;
     int qt = L - bh * p.nqt;
     if (CAUSAL) qt = p.nqt - 1 - qt;   // heaviest query tiles first
@@ -573,7 +581,7 @@ __global__ __launch_bounds__(512) void attn_fwd_dp_kernel(Params p) {
     const bool lag = wave >= NW / 2;
     const int g = lane >> 5, l32 = lane & 31;
     int L = blockIdx.x;
-    if (p.xcd_remap) L = (blockIdx.x & 7) * (p.num_wg >> 3) + (blockIdx.x >> 3);
+    if (p.xcd_remap) L = xcd_order(blockIdx.x, p.num_wg, p.xcd_remap);
     const int bh = L / p.nqt;
     int qt = L - bh * p.nqt;
     if (CAUSAL) qt = p.nqt - 1 - qt;
@@ -819,7 +827,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
     const int g = lane >> 5, l32 = lane & 31;
 
     int L = blockIdx.x;
-    if (p.xcd_remap) L = (blockIdx.x & 7) * (p.num_wg >> 3) + (blockIdx.x >> 3);
+    if (p.xcd_remap) L = xcd_order(blockIdx.x, p.num_wg, p.xcd_remap);
     const int bh = L / p.nqt;
     int qt = L - bh * p.nqt;
     if (CAUSAL) qt = p.nqt - 1 - qt;   // heaviest query tiles first
@@ -1114,11 +1122,16 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
 // P' for the P.V product is rounded to E4M3 (for either input format: the matrix core takes a
 // format per operand, and E4M3 keeps one more mantissa bit of the probabilities than E5M2).  Its
 // range is kept away from both ends of E4M3:
-//   * headroom: the running offset m is set to a row's max minus 8, so the largest P' of the tile
-//     that sets it is 2^8 = 256 and keys 17 binades below it are still representable (E4M3's
-//     smallest subnormal is 2^-9).  m moves only when a later tile's P' would pass 2^8.75 (E4M3's
-//     largest finite value is 448 = 2^8.81): the tile's lane max of the exponents is checked every
-//     tile, and a raise puts that tile's max back at 2^8.
+//   * headroom: the running offset m is set to the row max of the exponents (below) minus 5, so
+//     the largest P' of the tile that sets it is exactly 2^5 = 32 (its weight carries no rounding
+//     error, which matters for rows with few keys), keys 11 binades below it are still normal and
+//     14 binades below still representable (E4M3's smallest normal is 2^-6, its smallest subnormal
+//     2^-9).  m moves only when a later tile's P' leaves E4M3's range: a value above 464 converts
+//     to NaN, which the matrix core's row sum of P' (formed anyway) carries, and only then is the
+//     tile redone with its max put back at 2^5.  The slack of 2^3.86 (less up to one binade of the
+//     V mantissa below) is passed by about 3% of wave-tiles on N(0,1) scores; with 2^8 instead,
+//     the first tile's max (about 1.5 binades below a row's final max) left too little slack and
+//     half of all wave-tiles had to be redone.
 //   * V's descale never shifts P': vd_t = f_t * 2^e_t with f_t in [0.5, 1).  2^e_t is the E8M0
 //     block scale of the V^T operand of the scaled MFMA (the matrix core applies it exactly), and
 //     only log2(f_t), in [-1, 0), enters the exponent of P'.  So P' = exp2(x + log2 f_t - m), the
@@ -1126,8 +1139,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
 //     (A descale below 2^-126 is taken as 2^-126 with f_t = 1: such a block's V values are below
 //     448 * 2^-126 in magnitude, so the difference is below 6e-36.)
 
-// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales; operand format 0 = E4M3,
-// 1 = E5M2).  It sums A[i][k] B[k][j] over
+// MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 (operand format 0 = E4M3, 1 = E5M2; block scales 2^0
+// except on the V^T operand, which carries the power of two of V's descale).  It sums
+// A[i][k] B[k][j] over
 // the pairs (lane half, byte) that A and B share, so any key order that both operands use is
 // valid.  The order used here is the one of the S^T accumulator: byte b of lane half g of
 // k-step kk is key 64 kk + 32 (b / 16) + 8 ((b % 16) / 4) + 4 g + b % 4, so P^T is packed
@@ -1161,10 +1175,9 @@ __device__ __forceinline__ f32x16 mfma_f8_sa(const i32x8 &a, const i32x8 &b, con
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, 127);
 }
 
-// P' headroom: the tile that sets the running offset m puts its largest P' at 2^P8_HEAD; m moves
-// again only when a P' would pass 2^P8_LIMIT (448 = 2^8.807 is E4M3's largest finite value)
-constexpr float P8_HEAD = 8.0f;
-constexpr float P8_LIMIT = 8.75f;
+// P' headroom: the tile that sets the running offset m puts its largest P' at 2^P8_HEAD (E4M3's
+// largest finite value is 448 = 2^8.81, its smallest subnormal 2^-9)
+constexpr float P8_HEAD = 5.0f;
 
 // four floats -> four E4M3 bytes (round to nearest even), first value in the low byte.  The
 // first conversion's "old" operand only supplies bytes 2-3, which the second one overwrites, so
@@ -1204,7 +1217,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
     const int g = lane >> 5, l32 = lane & 31;
 
     int L = blockIdx.x;
-    if (p.xcd_remap) L = (blockIdx.x & 7) * (p.num_wg >> 3) + (blockIdx.x >> 3);
+    if (p.xcd_remap) L = xcd_order(blockIdx.x, p.num_wg, p.xcd_remap);
     const int bh = L / p.nqt;
     int qt = L - bh * p.nqt;
     if (CAUSAL) qt = p.nqt - 1 - qt;
@@ -1258,8 +1271,9 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
     n_full = min(n_full, n_total);
 
     const uint32_t smem0 = lds_addr(&smem[0][0][0]);
+    auto stage = [&](int t) __attribute__((always_inline)) { return smem0 + (uint32_t)((t % NS) * 2 * TILEB); };
     auto dma = [&](int t) __attribute__((always_inline)) {
-        const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
+        const uint32_t st = stage(t);
         load_kv_tile<BPW, BC, ROWB>(Kh, Vh, t * BC, Sk, goff, st, st + TILEB, wave);
     };
 
@@ -1267,56 +1281,78 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
     const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
 
-    auto compute = [&](int t, uint32_t kt, uint32_t vt, bool masked) __attribute__((always_inline)) {
-        const int k0 = t * BC;
-        // one address per lane offset and tile (stage base + lane offset), passed through an empty
-        // asm so that the compiler neither keeps every (offset + immediate) sum live across the loop
-        // nor re-derives the stage base per fetch: each fetch is that address + an immediate
-        uint32_t ka[2 * KSTEPS], va[D / 32];
+    // descales through the constant address space: wave-uniform scalar loads, which the
+    // vector-memory counter that paces the K/V pipeline does not see.  Tile t+1's are loaded at the
+    // end of tile t: a scalar load still in flight when the next K operand fetches are waited for
+    // would make that wait cover every LDS read too (scalar loads return out of order).
+    typedef const __attribute__((address_space(4))) float cfloat;
+    auto load_descales = [&](int t, float &kd, float &vd) __attribute__((always_inline)) {
+        const int tt = min(t, p.nkb - 1);
+        kd = p.kd ? ((cfloat *)p.kd)[(size_t)bh * p.nkb + tt] : 1.f;
+        vd = p.vd ? ((cfloat *)p.vd)[(size_t)bh * p.nkb + tt] : 1.f;
+    };
+    float kd_cur, vd_cur;
+
+    // The key loop is software-pipelined by one tile: iteration t forms S^T(t) and P'(t), and
+    // multiplies P'(t-1) into O.  The P'(t-1) products do not depend on tile t's softmax, so the
+    // matrix core runs them while the VALU forms P'(t); and the range check of P'(t-1) (below)
+    // reads a row sum that finished during the previous iteration.  The V tile of t-1 is still read
+    // in iteration t, so tiles are loaded two iterations ahead into four LDS stages.
+    static_assert(NS == 4, "the pipelined key loop needs four stages");
+
+    // per-tile scale terms: ct multiplies the raw code products; vsc / vf split V's descale
+    struct TileScale {
+        float ct, lvf, ivf;
+        int vsc;
+    };
+    auto decode = [&](float kdt, float vdt) __attribute__((always_inline)) {
+        // vd_t = vf * 2^(vsc - 127) with vf in [0.5, 1) (see the header above)
+        const uint32_t vbits = __float_as_uint(vdt);
+        const int vexp = (int)((vbits >> 23) & 0xff);
+        TileScale ts;
+        ts.vsc = vexp == 0 ? 1 : min(vexp + 1, 254);
+        const float vf = __uint_as_float(
+            vexp == 0 ? 0x3f800000u : ((vbits & 0x807fffffu) | (vexp >= 254 ? (127u << 23) : (126u << 23))));
+        ts.ct = cq * kdt;
+        ts.lvf = __builtin_amdgcn_logf(vf);   // log2(vf), in [-1, 0]
+        ts.ivf = __builtin_amdgcn_rcpf(vf);
+        return ts;
+    };
+
+    // S^T = K Q^T (codes) of the tile at LDS address kt, masked on diagonal and tail tiles
+    auto qk = [&](f32x16 (&s)[BC / 32], uint32_t kt, int t, bool masked) __attribute__((always_inline)) {
+        // one address per lane offset (stage base + lane offset), passed through an empty asm so
+        // that each fetch is that address + an immediate
+        uint32_t ka[2 * KSTEPS];
 #pragma unroll
         for (int j = 0; j < 2 * KSTEPS; ++j) {
             ka[j] = kt + (uint32_t)koff[j];
             asm volatile("" : "+v"(ka[j]));
         }
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            va[db] = vt + (uint32_t)vlane[db];
-            asm volatile("" : "+v"(va[db]));
-        }
-        // descales through the constant address space: wave-uniform scalar loads, which the
-        // vector-memory counter that paces the K/V pipeline does not see
-        typedef const __attribute__((address_space(4))) float cfloat;
-        const float kdt = p.kd ? ((cfloat *)p.kd)[(size_t)bh * p.nkb + t] : 1.f;
-        const float vdt = p.vd ? ((cfloat *)p.vd)[(size_t)bh * p.nkb + t] : 1.f;
-        // S^T = K Q^T (codes)
-        f32x16 s[BC / 32];
-#pragma unroll
         for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
         // S^T MFMAs in a fixed order, each fenced, with the K fetches of the next two in flight
-        // (0.5-1% faster than the compiler's order on the fp8 workloads; a ring of four was slower)
-        {
-            constexpr int NQK = KSTEPS * (BC / 32), RING = 2;
-            auto kread = [&](auto J) __attribute__((always_inline)) {
-                constexpr int jj = decltype(J)::value, ks = jj / (BC / 32), kb2 = jj % (BC / 32);
-                const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks]);
-                const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks + 1]);
-                return __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-            };
-            i32x8 ring[RING];
-            static_for<RING>([&](auto J) { ring[decltype(J)::value] = kread(J); });
+        constexpr int NQK = KSTEPS * (BC / 32), RING = 2;
+        auto kread = [&](auto J) __attribute__((always_inline)) {
+            constexpr int jj = decltype(J)::value, ks = jj / (BC / 32), kb2 = jj % (BC / 32);
+            const u32x4 lo = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks]);
+            const u32x4 hi = lds_load_b128<kb2 * 32 * ROWB>(ka[2 * ks + 1]);
+            return __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        };
+        i32x8 ring[RING];
+        static_for<RING>([&](auto J) { ring[decltype(J)::value] = kread(J); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NQK>([&](auto J) {
+            constexpr int jj = decltype(J)::value, ks = jj / (BC / 32), kb2 = jj % (BC / 32);
+            const i32x8 a = ring[jj % RING];
+            if constexpr (jj + RING < NQK) ring[jj % RING] = kread(std::integral_constant<int, jj + RING>{});
+            s[kb2] = mfma_f8<FMT, FMT>(a, qf[ks], s[kb2]);
             __builtin_amdgcn_sched_barrier(0);
-            static_for<NQK>([&](auto J) {
-                constexpr int jj = decltype(J)::value, ks = jj / (BC / 32), kb2 = jj % (BC / 32);
-                const i32x8 a = ring[jj % RING];
-                if constexpr (jj + RING < NQK) ring[jj % RING] = kread(std::integral_constant<int, jj + RING>{});
-                s[kb2] = mfma_f8<FMT, FMT>(a, qf[ks], s[kb2]);
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        }
+        });
         if (masked) {
-            const int base = k0 + 4 * g;
+            const int base = t * BC + 4 * g;
             int lim = Sk - base;
             if (CAUSAL) lim = min(lim, qw0 + l32 + 1 - base);
 #pragma unroll
@@ -1325,96 +1361,73 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
                 for (int i = 0; i < 16; ++i)
                     if (kb2 * 32 + 8 * (i >> 2) + (i & 3) >= lim) s[kb2][i] = -INFINITY;
         }
-        // V's descale: vd_t = vf * 2^(vsc - 127) with vf in [0.5, 1) (see the header above)
-        const uint32_t vbits = __float_as_uint(vdt);
-        const int vexp = (int)((vbits >> 23) & 0xff);
-        int vsc;
-        float vf;
-        if (vexp == 0) {
-            vsc = 1;
-            vf = 1.f;
-        } else if (vexp >= 254) {
-            vsc = 254;
-            vf = __uint_as_float((vbits & 0x807fffffu) | (127u << 23));
-        } else {
-            vsc = vexp + 1;
-            vf = __uint_as_float((vbits & 0x807fffffu) | (126u << 23));
+    };
+    auto raise_max = [&](float mnew) __attribute__((always_inline)) {
+        const float alpha = __builtin_amdgcn_exp2f(mrow - (mnew == -INFINITY ? 0.f : mnew));
+        mrow = mnew;
+        lrow *= alpha;
+        lrnd *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    };
+    // four independent chains from -inf (a max3 chain with no canonicalising first step)
+    auto lane_max = [&](const f32x16 (&s)[BC / 32]) __attribute__((always_inline)) {
+        float mq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float m0 = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s[k][i]);
+            mq[k] = m0;
         }
-        // online softmax of the base-2 exponents y = raw * ct + log2(vf).  The first tile sets the
-        // running offset m = (row max of y) - P8_HEAD.  Later tiles form x = y - m in place and
-        // p' = exp2(x) at once; the lane max of x is checked against P8_LIMIT, and only a wave
-        // where some lane passes it moves m (x's row max back to P8_HEAD) and forms P' again.
-        const float ct = cq * kdt;
-        const float lvf = __builtin_amdgcn_logf(vf);   // log2(vf), in [-1, 0]
-        const float ivf = __builtin_amdgcn_rcpf(vf);
-        auto raise_max = [&](float mnew) __attribute__((always_inline)) {
-            const float alpha = __builtin_amdgcn_exp2f(mrow - (mnew == -INFINITY ? 0.f : mnew));
-            mrow = mnew;
-            lrow *= alpha;
-            lrnd *= alpha;
+        return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    };
+    // x = raw * ct + log2(vf) - m in place
+    auto to_exponents = [&](f32x16 (&s)[BC / 32], const TileScale &ts) __attribute__((always_inline)) {
+        const float off = ts.lvf - ((mrow == -INFINITY) ? 0.f : mrow);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+        for (int kb2 = 0; kb2 < BC / 32; ++kb2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        };
-        auto lane_max = [&]() __attribute__((always_inline)) {
-            float mq[4];
+            for (int i = 0; i < 16; ++i) s[kb2][i] = __builtin_fmaf(s[kb2][i], ts.ct, off);
+    };
+    // P'^T in E4M3 from x: dword w of k-step kk = keys of s[2 kk + w / 4][4 (w % 4) .. + 3]; returns
+    // this lane's fp32 sum of p'
+    auto exp_pack = [&](const f32x16 (&s)[BC / 32], i32x8 (&pf)[BC / 64]) __attribute__((always_inline)) {
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float m0 = fmaxf(s[k][0], s[k][1]);
+        for (int kk = 0; kk < BC / 64; ++kk)
 #pragma unroll
-                for (int i = 2; i < 16; ++i) m0 = fmaxf(m0, s[k][i]);
-                mq[k] = m0;
-            }
-            return fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-        };
-        if (t == 0) raise_max(fmaxf(mrow, __builtin_fmaf(xhalf_max(lane_max()), ct, lvf) - P8_HEAD));
-        {
-            const float off = lvf - ((mrow == -INFINITY) ? 0.f : mrow);
+            for (int w = 0; w < 8; ++w) {
+                const f32x16 &sv = s[2 * kk + (w >> 2)];
+                const int o = 4 * (w & 3);
+                float e[4];
 #pragma unroll
-            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb2][i] = __builtin_fmaf(s[kb2][i], ct, off);
-        }
-        const float xmax = (t == 0) ? 0.f : lane_max();
-        // P'^T in E4M3: dword w of k-step kk = keys of s[2 kk + w / 4][4 (w % 4) .. + 3]
-        i32x8 pf[BC / 64];
-        auto exp_pack = [&]() __attribute__((always_inline)) {
-            float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < BC / 64; ++kk)
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    const f32x16 &sv = s[2 * kk + (w >> 2)];
-                    const int o = 4 * (w & 3);
-                    float e[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        e[j] = __builtin_amdgcn_exp2f(sv[o + j]);
-                        ls[j] += e[j];
-                    }
-                    pf[kk][w] = pack4_e4m3(e[0], e[1], e[2], e[3]);
+                for (int j = 0; j < 4; ++j) {
+                    e[j] = __builtin_amdgcn_exp2f(sv[o + j]);
+                    ls[j] += e[j];
                 }
-            return (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        };
-        float lsum = exp_pack();
-        if (__builtin_amdgcn_ballot_w64(xmax > P8_LIMIT) != 0) {
-            const float rm = xhalf_max(xmax);
-            const float d = rm > P8_LIMIT ? rm - P8_HEAD : 0.f;
-            raise_max(mrow + d);
+                pf[kk][w] = pack4_e4m3(e[0], e[1], e[2], e[3]);
+            }
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    // sum of the rounded p' (the weights P.V uses) of each query: ones x P'^T on the matrix core
+    auto row_sum = [&](const i32x8 (&pf)[BC / 64]) __attribute__((always_inline)) {
+        f32x16 r = {};
 #pragma unroll
-            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+        for (int kk = 0; kk < BC / 64; ++kk) r = mfma_f8<0, 0>(ones, pf[kk], r);
+        return r[0];   // every row of ones x P'^T holds the same sums
+    };
+    // O^T += V^T P'^T for the V tile at LDS address vt: op (kk, db) needs four transposing fetches,
+    // issued PV_AHEAD ops ahead of their MFMA
+    auto pv = [&](const i32x8 (&pf)[BC / 64], uint32_t vt, int vsc) __attribute__((always_inline)) {
+        uint32_t va[D / 32];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb2][i] -= d;
-            lsum = exp_pack();
+        for (int db = 0; db < D / 32; ++db) {
+            va[db] = vt + (uint32_t)vlane[db];
+            asm volatile("" : "+v"(va[db]));
         }
-        lrow += lsum * ivf;
-        // sum of the rounded p' (the weights P.V uses): ones x P'^T on the matrix core
-        f32x16 rs = {};
-#pragma unroll
-        for (int kk = 0; kk < BC / 64; ++kk) rs = mfma_f8<0, 0>(ones, pf[kk], rs);
-        // O^T += V^T P'^T: op (kk, db) needs four transposing fetches; the fetches of PV_AHEAD
-        // later ops stay in flight ahead of each MFMA (a scheduling fence after every op keeps that)
         constexpr int NPV = (BC / 64) * (D / 32), PV_AHEAD = 2;
         auto pv_fetch = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value, kk = i / (D / 32), db = i % (D / 32);
@@ -1426,37 +1439,83 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
         };
         i32x8 ring[PV_AHEAD];
         static_for<PV_AHEAD>([&](auto J) { ring[decltype(J)::value] = pv_fetch(J); });
-        __builtin_amdgcn_sched_barrier(0);
         static_for<NPV>([&](auto J) {
             constexpr int j = decltype(J)::value, kk = j / (D / 32), db = j % (D / 32);
             const i32x8 a = ring[j % PV_AHEAD];
             if constexpr (j + PV_AHEAD < NPV) ring[j % PV_AHEAD] = pv_fetch(std::integral_constant<int, j + PV_AHEAD>{});
             oacc[db] = mfma_f8_sa<FMT, 0>(a, pf[kk], oacc[db], vsc);
-            __builtin_amdgcn_sched_barrier(0);
         });
-        lrnd += rs[0] * ivf;
     };
 
-    constexpr int LPT = 2 * BPW;
-    auto step = [&](int t, bool masked) __attribute__((always_inline)) {
-        const int ahead = min(NS - 2, n_total - 1 - t);
-        if (NS >= 4 && ahead >= 2)
-            wait_vmcnt<2 * LPT>();
-        else if (NS >= 3 && ahead >= 1)
+    // the tile waiting for its P.V product: its P'^T, sums and scale terms
+    i32x8 pprev[BC / 64];
+    float ls_prev = 0.f, rs_prev = 0.f;
+    TileScale ts_prev = {0.f, 0.f, 1.f, 127};
+    int t_prev = -1;
+
+    // Check the waiting tile: a NaN row sum means some P' passed E4M3's range (values above 464
+    // convert to NaN); then the tile's scores are formed again from its K tile (still in LDS), m
+    // moves up so that the tile's row max is at P8_HEAD, and P' is formed again.  O has not yet
+    // received this tile's products, so rescaling it and the sums is all the correction needs.
+    auto check_prev = [&]() __attribute__((always_inline)) {
+        if (__builtin_amdgcn_ballot_w64(rs_prev != rs_prev) != 0) {
+            f32x16 s[BC / 32];
+            qk(s, stage(t_prev), t_prev, true);   // the mask changes nothing on a full tile
+            to_exponents(s, ts_prev);
+            const float d = fmaxf(xhalf_max(lane_max(s)) - P8_HEAD, 0.f);
+            raise_max(mrow + d);
+#pragma unroll
+            for (int kb2 = 0; kb2 < BC / 32; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb2][i] -= d;
+            ls_prev = exp_pack(s, pprev);
+            rs_prev = row_sum(pprev);
+        }
+        lrow += ls_prev * ts_prev.ivf;
+        lrnd += rs_prev * ts_prev.ivf;
+    };
+    auto pv_prev = [&]() __attribute__((always_inline)) {
+        pv(pprev, stage(t_prev) + TILEB, ts_prev.vsc);
+        t_prev = -1;
+    };
+
+    // Tile t: the waiting tile's check, S^T(t), then P'(t-1) into O (the matrix core) while P'(t)
+    // is formed (the VALU).  The first tile of a row sets m from its row max.  A causal wave whose
+    // queries all precede the tile only finishes the waiting tile.
+    auto tile = [&](int t, bool masked, bool work) __attribute__((always_inline)) {
+        const bool waiting = t_prev >= 0;
+        if (waiting) check_prev();
+        const TileScale ts = decode(kd_cur, vd_cur);
+        f32x16 s[BC / 32];
+        if (work) {
+            qk(s, stage(t), t, masked);
+            if (t == 0) raise_max(__builtin_fmaf(xhalf_max(lane_max(s)), ts.ct, ts.lvf) - P8_HEAD);
+        }
+        if (waiting) pv_prev();
+        if (work) {
+            to_exponents(s, ts);
+            ls_prev = exp_pack(s, pprev);
+            rs_prev = row_sum(pprev);
+            ts_prev = ts;
+            t_prev = t;
+        }
+    };
+
+    // one iteration: wait until tile t has landed for every wave (this wave's loads of tile t+1 may
+    // still be in flight), which also means every wave is done with iteration t-1 and so with tile
+    // t-2, whose stage then receives tile t+2
+    auto step_begin = [&](int t) __attribute__((always_inline)) {
+        constexpr int LPT = 2 * BPW;   // direct-to-LDS loads per tile per wave
+        if (t + 1 < n_total)
             wait_vmcnt<LPT>();
         else
             wait_vmcnt<0>();
         wg_barrier();
-        if (t + NS - 1 < n_total) dma(t + NS - 1);
-        if (!masked || !CAUSAL || t * BC <= qw0 + 31) {
-            const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
-            compute(t, st, st + TILEB, masked);
-        }
+        if (t + 2 < n_total) dma(t + 2);
     };
 
-#pragma unroll
-    for (int u = 0; u < NS - 1; ++u)
-        if (u < n_total) dma(u);
+    dma(0);
+    if (n_total > 1) dma(1);
     {
         const int row = min(qw0 + l32, Sq - 1);
 #pragma unroll
@@ -1466,11 +1525,26 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
             qf[ks] = __builtin_bit_cast(i32x8, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         }
     }
+    load_descales(0, kd_cur, vd_cur);
     __builtin_amdgcn_s_waitcnt(0);
 
     int t = 0;
-    for (; t < n_full; ++t) step(t, false);
-    for (; t < n_total; ++t) step(t, true);
+    for (; t < n_full; ++t) {
+        step_begin(t);
+        tile(t, false, true);
+        load_descales(t + 1, kd_cur, vd_cur);
+    }
+    // diagonal and tail tiles: a causal wave whose queries all precede the tile has nothing to add
+    for (; t < n_total; ++t) {
+        step_begin(t);
+        tile(t, true, !CAUSAL || t * BC <= qw0 + 31);
+        load_descales(t + 1, kd_cur, vd_cur);
+    }
+    // the last tile's K and V stay in their stage: no load follows them
+    if (t_prev >= 0) {
+        check_prev();
+        pv_prev();
+    }
 
     // lrow holds this lane half's keys; lrnd already sums both halves (the MFMA reduces over k)
     const float lt = xhalf_sum(lrow);
@@ -1519,6 +1593,39 @@ int check_common(const void *q, const void *k, const void *v, const void *o, con
     return ATTN_OK;
 }
 
+// CU and XCD counts of the current device, queried once per device (the policy table below was
+// measured on 256 CUs in 8 XCDs; those are also the values taken when no device answers, e.g. for
+// a plan asked for on a host without one).
+struct DevInfo {
+    int cus, xcds;
+};
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DevInfo g_dev_info[kMaxDevices];
+
+DevInfo device_info() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return {256, 8};
+    }
+    std::call_once(g_dev_once[dev], [dev] {
+        int cus = 0, xcds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1) xcds = 8;
+        (void)hipGetLastError();
+        g_dev_info[dev] = {cus, xcds};
+    });
+    return g_dev_info[dev];
+}
+
+// XCD count to order workgroups by (see xcd_order), or 0 when the grid does not split evenly
+int xcd_remap_for(int num_wg) {
+    const int nx = device_info().xcds;
+    return (nx > 1 && num_wg % nx == 0) ? nx : 0;
+}
+
 // Schedules and tile shapes that are compiled: (schedule, query blocks per wave, waves, stages,
 // keys per tile).
 constexpr int kShapes[][5] = {
@@ -1565,7 +1672,9 @@ int policy_override() {
 // the classic schedule with 64 queries per wave (2, 8, 4) is 7% faster than with 32 (1, 8, 4) as
 // long as its 512-query workgroups fill the 256 CUs (slower on the tiny S=128 workload, which
 // they do not), except causal, where 128-key tiles (1, 8, 2) are 1.5% faster again; the
-// de-phased schedule is not faster there.
+// de-phased schedule is not faster there.  Choosing the kernel variant at run time from a table
+// measured per shape and keyed on the device's compute-unit count is the runtime policy of the
+// FlashInfer KDA write-up (blog.secrett2633), its section 1 and its closing lessons.
 void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
     pl->sched = ATTN_SCHED_CLASSIC;
     pl->qb = 1;
@@ -1576,7 +1685,7 @@ void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
     } else {
         pl->ns = 4;
         pl->bk = 64;
-        if ((long long)B * H * ((Sq + 511) / 512) >= 256) {
+        if ((long long)B * H * ((Sq + 511) / 512) >= device_info().cus) {
             pl->qb = 2;
             // causal at that size: 128-key tiles with 32 queries per wave are 1.5% faster still
             // (B=1 H=16 S=16384: 627.0 vs 636.7 us); non-causal they are 1.7% slower
@@ -1663,7 +1772,7 @@ int dispatch(const Params &p, const Plan &pl, int d, int causal, hipStream_t s) 
 
 // fp8: 8 waves x 32 queries, 128-key tiles (one descale block), two stages (measured 2-3% faster
 // than three or four on every fp8 workload: B2 H16 S4096 d128 184 vs 189 us, causal S8192 362 vs 371)
-constexpr int kFp8Stages = 2;
+constexpr int kFp8Stages = 4;
 
 void make_plan_fp8(int B, int H, int Sq, Plan *pl) {
     pl->sched = 0;
@@ -1713,7 +1822,7 @@ int run_fp8(const void *q, const void *k, const void *v, const float *q_descale,
     p.nkb = (S_k + 127) / 128;
     p.nqt = pl.nqt;
     p.num_wg = pl.num_wg;
-    p.xcd_remap = (pl.num_wg % 8 == 0) ? 1 : 0;
+    p.xcd_remap = xcd_remap_for(pl.num_wg);
     p.c = scale * 1.44269504088896340736f;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return fmt ? launch_fp8_d<1>(p, pl, d, causal, s) : launch_fp8_d<0>(p, pl, d, causal, s);
@@ -1752,7 +1861,7 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     p.Sk = S_k;
     p.nqt = pl.nqt;
     p.num_wg = pl.num_wg;
-    p.xcd_remap = (pl.num_wg % 8 == 0) ? 1 : 0;
+    p.xcd_remap = xcd_remap_for(pl.num_wg);
     p.c = scale * 1.44269504088896340736f;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == ATTN_BF16) return dispatch<BF16>(p, pl, d, causal, s);

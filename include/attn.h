@@ -55,8 +55,9 @@ typedef enum {
     ATTN_ERR_UNSUPPORTED = 3,  /* d not 64 or 128, or unknown dtype */
     ATTN_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned */
     ATTN_ERR_OVERFLOW = 5,     /* S*d or the grid size exceeds the 32-bit index range */
-    ATTN_ERR_VALUE = 6,        /* scale is not finite or not > 0 */
-    ATTN_ERR_LAUNCH = 7,       /* the HIP runtime refused the launch (no device, bad stream, ...) */
+    ATTN_ERR_LAUNCH = 6,       /* the HIP runtime refused the launch (no device, bad stream, ...) */
+    /* codes past the six of the original plan, for checks it did not foresee: */
+    ATTN_ERR_VALUE = 7,        /* scale (or the RMSNorm's eps) is not finite or out of range */
     ATTN_ERR_DESCALE = 8       /* fp8 path: a descale pointer is NULL or misaligned (4 bytes) */
 } attn_status;
 
@@ -159,6 +160,14 @@ int attn_quantize_qkv(const void *q, const void *k, const void *v, int dtype, in
  */
 int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, const void *w_k, void *q_out, void *k_out,
                     int B, int H, int S_q, int S_k, int d, float eps, int dtype, void *stream);
+
+/*
+ * Tile policy.  attn_fwd picks a compiled kernel variant (schedule and tile shape) at run time from
+ * a table measured on MI355X, keyed on the shape (d, causal, dtype, S_q, B*H) and on the device's
+ * compute-unit count, the runtime policy that the FlashInfer KDA write-up (blog.secrett2633)
+ * describes in its section 1 and its closing lessons.  The entry points below report that choice
+ * and override it (for tuning and tests); none of them touches device memory.
+ */
 
 /* Schedules of the f16/bf16 kernel (attn_fwd_set_policy). */
 typedef enum {

@@ -15,7 +15,7 @@ import exact_attention_32_amd as ea
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, OVERFLOW, VALUE, LAUNCH, DESCALE = range(9)
+OK, NULL, SHAPE, UNSUP, ALIGN, OVERFLOW, LAUNCH, VALUE, DESCALE = range(9)
 P = 0x10000   # a fake, 16-byte aligned "device pointer" (never dereferenced)
 
 
@@ -246,3 +246,25 @@ def test_quantize_qkv_validation(lib):
     assert callqkv(lib, fmt=0) == UNSUP and callqkv(lib, fmt=1) == UNSUP and callqkv(lib, fmt=3) == UNSUP
     assert callqkv(lib, d=96) == UNSUP and callqkv(lib, dtype=2) == UNSUP
     assert callqkv(lib, B=2 ** 16, H=2 ** 16, Sk=2 ** 10) == OVERFLOW
+
+
+def test_output_buffer_checks():
+    """The binding refuses a caller-supplied output the kernel would write past or into the wrong
+    memory: wrong shape, type, device or layout (checked before any library call)."""
+    import torch
+
+    import exact_attention_32_amd as ea
+
+    dev = torch.device("cpu")
+    good = torch.empty(2, 3, 5, 64, dtype=torch.bfloat16)
+    ea._check_buffer(good, "out", (2, 3, 5, 64), torch.bfloat16, dev)
+    bad = [
+        torch.empty(2, 3, 4, 64, dtype=torch.bfloat16),                       # too few rows
+        torch.empty(2, 3, 5, 64, dtype=torch.float16),                        # wrong type
+        torch.empty(2, 3, 64, 5, dtype=torch.bfloat16).transpose(2, 3),       # not dense
+        torch.empty(2, 3, 5, 64, dtype=torch.bfloat16, device="meta"),        # another device
+        None,
+    ]
+    for t in bad:
+        with pytest.raises(ValueError):
+            ea._check_buffer(t, "out", (2, 3, 5, 64), torch.bfloat16, dev)

@@ -439,3 +439,31 @@ def test_fp8_range(oracle, kind, fmt):
             gate = 5e-2 * (max(1.0, float(np.abs(ro).max())) if kind.startswith("vspread") else 1.0)
             U.say(f"   max|dO| {err_o:.3e} (gate {gate:.3e}, max|O| {np.abs(ro).max():.3e}), max|dLSE| {err_l:.3e}")
             assert np.all(np.isfinite(og)) and err_o <= gate and err_l <= U.TOL_LSE, (kind, fmt, d, causal)
+
+
+def test_binding_rejects_bad_outputs(oracle):
+    """fwd / fwd_fp8 / quantize_fp8 refuse outputs of the wrong size, type, device or layout (before
+    any launch), and the same call with correct outputs then runs."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    U.say("[gpu] binding output checks")
+    q = torch.randn(1, 2, 70, 64, device=dev).to(torch.bfloat16)
+    for out, lse in ((torch.empty(1, 2, 69, 64, dtype=torch.bfloat16, device=dev), None),
+                     (torch.empty(1, 2, 70, 64, dtype=torch.float16, device=dev), None),
+                     (torch.empty(1, 2, 70, 64, dtype=torch.bfloat16), None),
+                     (None, torch.empty(1, 2, 69, dtype=torch.float32, device=dev)),
+                     (None, torch.empty(1, 2, 70, dtype=torch.float32))):
+        with pytest.raises(ValueError):
+            ea.fwd(q, q, q, out=out, lse=lse)
+    c = torch.zeros(1, 2, 70, 64, dtype=torch.uint8, device=dev)
+    ds = torch.ones(1, 2, 1, device=dev)
+    with pytest.raises(ValueError):
+        ea.fwd_fp8(c, c, c, ds, ds, ds.cpu())
+    with pytest.raises(ValueError):
+        ea.fwd_fp8(c, c, c, ds, ds, ds, out=torch.empty(1, 2, 70, 64, dtype=torch.float16, device=dev))
+    with pytest.raises(ValueError):
+        ea.quantize_fp8(q.float(), codes=torch.empty(1, 2, 70, 64, dtype=torch.uint8))
+    o, lse = ea.fwd(q, q, q, out=torch.empty(1, 2, 70, 64, dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
