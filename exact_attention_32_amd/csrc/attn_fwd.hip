@@ -127,6 +127,7 @@ struct Params {
     int num_wg;      // total workgroups
     int xcd_remap;   // XCD count nx: map workgroups so each XCD gets a contiguous range of heads; 0: off
     float c;         // scale * log2(e)
+    int pair;        // causal, classic schedule: a workgroup takes query tiles nqt-1-j and j (see there)
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -154,6 +155,14 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 // loads of later tiles).  The LDS data a wave needs is covered by its explicit memory-counter
 // wait before the barrier; the empty asm statements keep the compiler from moving memory
 // accesses across it.
+// The lane id, formed where it is used: the compiler can neither hoist it out of a loop nor keep
+// it (or an address made from it) in a register across one.
+__device__ __forceinline__ int fresh_lane_id() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -250,21 +259,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
 
+    // Work item L: one query tile, or (causal, p.pair) the pair of tiles nqt-1-j and j of one head,
+    // the heavy one first with the key tiles in order, then the light one with them in reverse
+    // order.  Both passes of a pair together take the same number N of key-tile steps for every j,
+    // so the workgroups of a head that start together finish together, and at step u all of them
+    // read the same key tile: tile u in the first pass, tile N-1-u in the second.  Unpaired, the
+    // causal tiles run heaviest first, and a tile that starts when another ends reads its keys one
+    // query tile's worth of steps behind the tile that started before it on that XCD.  A key tile
+    // that the first and the second pass both read is still fetched twice when the two reads lie
+    // far apart (bf16 causal B=1 H=32 S=8192 d=128: FETCH_SIZE 1.25x the algorithmic bytes paired,
+    // 1.43x unpaired).
     int L = blockIdx.x;
     if (p.xcd_remap) L = xcd_order(blockIdx.x, p.num_wg, p.xcd_remap);
-    const int bh = L / p.nqt;
-    int qt = L - bh * p.nqt;
-    if (CAUSAL) qt = p.nqt - 1 - qt;   // heaviest query tiles first
-    const int q0 = qt * BR;
+    const int np = (CAUSAL && p.pair) ? (p.nqt + 1) >> 1 : p.nqt;
+    const int bh = L / np;
+    const int jq = L - bh * np;
+    const int npass = (CAUSAL && p.pair && 2 * jq + 1 != p.nqt) ? 2 : 1;
     const int Sq = p.Sq, Sk = p.Sk;
 
     const uint16_t *__restrict__ Qh = p.q + (size_t)bh * Sq * D;
     const uint16_t *__restrict__ Kh = p.k + (size_t)bh * Sk * D;
     const uint16_t *__restrict__ Vh = p.v + (size_t)bh * Sk * D;
-
-    const int qw0 = q0 + wave * QB * 32;   // first query of this wave
-
-    u32x4 qf[QB][D / 16];   // Q^T operands, loaded after the first K/V loads are issued
 
     // per-lane LDS offsets of the MFMA operand fetches (the swizzle only sees row bits 0..3)
     int koff[D / 16];
@@ -296,6 +311,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         goff[j] = (uint32_t)(grow[j] * ROWB + gcolb[j]);
     }
 
+    for (int pass = 0; pass < npass; ++pass) {
+    const int qt = CAUSAL ? (pass == 0 ? p.nqt - 1 - jq : jq) : jq;   // causal: heaviest tiles first
+    const bool rev = CAUSAL && pass == 1;                             // keys in reverse order
+    const int q0 = qt * BR;
+    const int qw0 = q0 + wave * QB * 32;   // first query of this wave
+
+    u32x4 qf[QB][D / 16];   // Q^T operands, loaded after the first K/V loads are issued
+
     f32x16 oacc[QB][D / 32];
     float mrow[QB], lrow[QB], lrnd[QB];
 #pragma unroll
@@ -317,16 +340,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         n_full = min(n_full, (q0 + 1) / BC);
     }
     n_full = min(n_full, n_total);
+    // step u takes key tile tile_of(u) from LDS stage u % NS
+    auto tile_of = [&](int u) __attribute__((always_inline)) { return rev ? n_total - 1 - u : u; };
+    // the step that sets the running max: the wave's first tile with keys for it (in reverse order,
+    // the last tile it sees at all; its rows each see at least the key of their own position there)
+    const int u_first = rev ? n_total - 1 - min(n_total - 1, (qw0 + QB * 32 - 1) / BC) : 0;
 
     const uint32_t smem0 = lds_addr(&smem[0][0][0]);
-    auto dma = [&](int t) __attribute__((always_inline)) {
-        const uint32_t st = smem0 + (uint32_t)((t % NS) * 2 * TILEB);
-        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, t * BC, Sk, goff, st,
-                                    st + TILEB, wave);
+    auto dma = [&](int u) __attribute__((always_inline)) {
+        const uint32_t st = smem0 + (uint32_t)((u % NS) * 2 * TILEB);
+        load_kv_tile<BPW, BC, ROWB>((const unsigned char *)Kh, (const unsigned char *)Vh, tile_of(u) * BC, Sk, goff,
+                                    st, st + TILEB, wave);
     };
 
     const float c = p.c;
-    auto compute = [&](int t, const unsigned char *kb, const unsigned char *vb, bool masked)
+    auto compute = [&](int t, bool first, const unsigned char *kb, const unsigned char *vb, bool masked)
                        __attribute__((always_inline)) {
         const int k0 = t * BC;
         // S^T = K Q^T
@@ -358,7 +386,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
-        if (masked) {
+        if (masked && (k0 + BC > Sk || (CAUSAL && k0 + BC - 1 > qw0))) {
             // element i of block kb2 holds key k0 + 4g + c with c = 32 kb2 + 8 (i / 4) + i % 4 (a
             // constant); it is visible iff c < lim
 #pragma unroll
@@ -426,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb2][i]);
             return xhalf_max(mx);
         };
-        if (t == 0) {
+        if (first) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) raise_max(qb, fmaxf(mrow[qb], row_max(qb) * c));
         }
@@ -499,11 +527,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 
     constexpr int LPT = 2 * BPW;   // direct-to-LDS loads per tile per wave
 
-    // one tile: wait until tile t is in LDS for every wave (this wave's loads of the next tiles
-    // may still be in flight), which also means every wave is done with tile t-1, whose stage
-    // then receives tile t+NS-1; compute on tile t
-    auto step = [&](int t, bool masked) __attribute__((always_inline)) {
-        const int ahead = min(NS - 2, n_total - 1 - t);   // tiles issued after t
+    // step u: wait until its tile is in LDS for every wave (this wave's loads of the next tiles
+    // may still be in flight), which also means every wave is done with step u-1, whose stage
+    // then receives the tile of step u+NS-1; compute on the tile
+    auto step = [&](int u, bool masked) __attribute__((always_inline)) {
+        const int ahead = min(NS - 2, n_total - 1 - u);   // tiles issued after this one
         if (NS >= 4 && ahead >= 2)
             wait_vmcnt<2 * LPT>();
         else if (NS >= 3 && ahead >= 1)
@@ -511,53 +539,64 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         else
             wait_vmcnt<0>();
         wg_barrier();
-        if (t + NS - 1 < n_total) dma(t + NS - 1);
+        if (u + NS - 1 < n_total) dma(u + NS - 1);
         // causal: a wave whose queries all precede the tile has nothing to add
+        const int t = tile_of(u);
         if (!masked || !CAUSAL || t * BC <= qw0 + QB * 32 - 1)
-            compute(t, &smem[t % NS][0][0], &smem[t % NS][1][0], masked);
+            compute(t, u == u_first, &smem[u % NS][0][0], &smem[u % NS][1][0], masked);
     };
 
+    // the second pass: every wave is done with the first pass's last tile before its stages refill
+    if (pass) wg_barrier();
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u)
         if (u < n_total) dma(u);
     // Q^T operands (B of the S^T MFMA), resident for the whole key loop.  Rows past S_q are
     // clamped: they are computed and never stored.
+    {
+        const int lq = fresh_lane_id();
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = min(qw0 + qb * 32 + l32, Sq - 1);
+        for (int qb = 0; qb < QB; ++qb) {
+            const int row = min(qw0 + qb * 32 + (lq & 31), Sq - 1);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            qf[qb][ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
+            for (int ks = 0; ks < D / 16; ++ks)
+                qf[qb][ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + (lq >> 5) * 8);
+        }
     }
 
     // the Q fragments are the newest loads; draining them here keeps the in-order memory
     // counter free of them inside the key loop
     __builtin_amdgcn_s_waitcnt(0);
 
-    int t = 0;
-    for (; t < n_full; ++t) step(t, false);
-    for (; t < n_total; ++t) step(t, true);
+    // the tiles without a mask, then those with one (the causal diagonal or the S_k tail); in
+    // reverse order every step takes the masked form, which skips the mask where the tile needs none
+    int u = 0;
+    for (; u < (rev ? 0 : n_full); ++u) step(u, false);
+    for (; u < n_total; ++u) step(u, true);
 
     // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
+    const int lane_e = fresh_lane_id();
+    const int ge = lane_e >> 5;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float lt = xhalf_sum(lrow[qb]);
         const float inv = 1.0f / xhalf_sum(lrnd[qb]);
-        const int qrow = qw0 + qb * 32 + l32;
+        const int qrow = qw0 + qb * 32 + (lane_e & 31);
         if (qrow < Sq) {
             uint16_t *orow = p.o + ((size_t)bh * Sq + qrow) * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int gi = 0; gi < 4; ++gi) {
-                    const int dv = db * 32 + 8 * gi + 4 * g;
+                    const int dv = db * 32 + 8 * gi + 4 * ge;
                     u32x2 val = u32x2{pack2<T>(oacc[qb][db][gi * 4 + 0] * inv, oacc[qb][db][gi * 4 + 1] * inv),
                                       pack2<T>(oacc[qb][db][gi * 4 + 2] * inv, oacc[qb][db][gi * 4 + 3] * inv)};
                     *reinterpret_cast<u32x2 *>(orow + dv) = val;
                 }
-            if (p.lse && g == 0) p.lse[(size_t)bh * Sq + qrow] = (mrow[qb] + log2f(lt)) * 0.69314718055994530942f;
+            if (p.lse && ge == 0) p.lse[(size_t)bh * Sq + qrow] = (mrow[qb] + log2f(lt)) * 0.69314718055994530942f;
         }
     }
+    }   // pass
 }
 
 // De-phased schedule for two waves per SIMD: 8 waves of 32 queries, 64-key tiles, 4 LDS stages,
@@ -1572,6 +1611,7 @@ struct Plan {
     int sched;                   // ATTN_SCHED_CLASSIC, _PINGPONG or _DEPHASED (f16/bf16); 0 for fp8
     int qb, nw, ns, bk;          // 32-query blocks per wave, waves, LDS stages, keys per tile
     int block_q, block_k, nqt, num_wg;
+    int pair;                    // causal classic schedule: one workgroup per pair of query tiles
 };
 
 // Internal status of check_common: no query rows (B, H or S_q = 0), so nothing to compute.
@@ -1720,7 +1760,12 @@ int make_plan(int B, int H, int Sq, int d, int causal, Plan *pl) {
     pl->block_q = pl->nw * pl->qb * 32;
     pl->block_k = pl->bk;
     pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
-    const long long wg = (long long)pl->nqt * B * H;
+    // Causal tiles go in pairs (nqt-1-j, j) when the pairs alone still give every CU a workgroup:
+    // the key tiles are then fetched about once per head instead of up to twice (bf16 causal
+    // B=1 H=32 S=8192 d=128: FETCH_SIZE 1.33x the algorithmic bytes unpaired).
+    const long long npair = (long long)B * H * ((pl->nqt + 1) / 2);
+    pl->pair = causal && pl->sched == ATTN_SCHED_CLASSIC && pl->nqt >= 2 && npair >= device_info().cus;
+    const long long wg = pl->pair ? npair : (long long)pl->nqt * B * H;
     if (wg > INT_MAX) return ATTN_ERR_OVERFLOW;
     pl->num_wg = (int)wg;
     return ATTN_OK;
@@ -1780,6 +1825,7 @@ void make_plan_fp8(int B, int H, int Sq, Plan *pl) {
     pl->qb = 1;
     pl->nw = 8;
     pl->ns = kFp8Stages;
+    pl->pair = 0;
     pl->block_q = 256;
     pl->block_k = 128;
     pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
@@ -1863,6 +1909,7 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     p.num_wg = pl.num_wg;
     p.xcd_remap = xcd_remap_for(pl.num_wg);
     p.c = scale * 1.44269504088896340736f;
+    p.pair = pl.pair;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == ATTN_BF16) return dispatch<BF16>(p, pl, d, causal, s);
     return dispatch<F16>(p, pl, d, causal, s);

@@ -209,6 +209,18 @@ def test_set_policy(lib):
     assert ea.plan(1, 2, 129, 128, 64, False)[:3] == (256, 64, 8)
 
 
+def test_plan_causal_pairs(lib):
+    """Causal problems whose tile pairs still give every CU a workgroup launch one per pair of
+    query tiles (n-1-j, j); smaller ones, non-causal ones and fp8 one per tile.  (Here, without a
+    device, the CU count is the 256 the table was measured on.)"""
+    assert ea.plan(1, 32, 8192, 8192, 128, True) == (256, 128, 8, 32 * 16)
+    assert ea.plan(1, 16, 16384, 16384, 64, True) == (256, 128, 8, 16 * 32)
+    assert ea.plan(2, 43, 1200, 1200, 128, True)[3] == 2 * 43 * 3   # 5 tiles: 2 pairs and 1 alone
+    assert ea.plan(1, 32, 8192, 8192, 128, False)[3] == 32 * 32
+    assert ea.plan(1, 2, 1024, 1024, 128, True)[3] == 2 * 4   # 4 pairs would leave CUs idle
+    assert ea.plan(1, 32, 8192, 8192, 128, True, dtype=ea.ATTN_FP8_E4M3)[3] == 32 * 32
+
+
 def callqn(lib, q=P, k=P, wq=P, wk=P, qo=P, ko=P, B=1, H=2, Sq=16, Sk=16, d=128, eps=1e-6, dtype=1):
     return lib.attn_qk_rmsnorm(q, k, wq, wk, qo, ko, B, H, Sq, Sk, d, eps, dtype, None)
 

@@ -115,6 +115,44 @@ def test_every_schedule(oracle, sched):
         ea.set_policy(ea.ATTN_SCHED_DEFAULT)
 
 
+# causal shapes whose (batch, head) count makes the library pair query tiles (n-1-j, j) in one
+# workgroup, the light tile with its keys in reverse order: even and odd tile counts (an odd one
+# leaves the middle tile alone), S_q < S_k and S_q > S_k, both head dimensions and tile shapes
+PAIRED = [(1, 128, 1024, 1024, 64), (2, 43, 1200, 1200, 128), (1, 128, 1000, 1100, 128), (1, 100, 1300, 900, 64)]
+
+
+@pytest.mark.parametrize("shape", PAIRED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_causal_pairs(oracle, shape, dtype):
+    import exact_attention_32_amd as ea
+
+    B, H, Sq, Sk, d = shape
+    bq, bk, w_, n = ea.plan(B, H, Sq, Sk, d, True)
+    nqt = -(-Sq // bq)
+    assert n == B * H * ((nqt + 1) // 2), (shape, bq, n)   # paired
+    w = I.random_workload(B, H, Sq, Sk, d, dtype, True, seed=4000 + Sq + 7 * Sk + d + H)
+    st = _run_full(oracle, w)
+    assert st["pass"], st
+
+
+@pytest.mark.parametrize("kind", ["ramp12", "step40", "step150"])
+def test_causal_pairs_rising(oracle, kind):
+    """Rising scores through paired causal tiles: the heavy tile raises its running max as the
+    keys go up, the light tile (keys in reverse order) starts from its largest scores."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    for d, dtype in ((64, "bf16"), (128, "f16")):
+        q, k, v = _rising_inputs(kind, 1, 128, 1024, d, dtype, seed=d + 11)
+        assert ea.plan(1, 128, 1024, 1024, d, True)[3] == 128 * 2
+        U.say(f"[gpu] pairs rising {kind} d={d} {dtype}")
+        o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=True, scale=d ** -0.5)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), True, d ** -0.5)
+        st = U.compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, dtype)
+        assert st["pass"], (kind, d, dtype, st)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_outliers_small(oracle, causal):
     w = I.random_workload(1, 2, 700, 700, 64, "bf16", causal, seed=55, outliers=True)
