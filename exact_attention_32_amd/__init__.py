@@ -57,6 +57,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     L.attn_quantize_qkv.argtypes = [vp, vp, vp, ci, ci] + [vp] * 6 + [ci] * 5 + [vp]
     L.attn_qk_rmsnorm.restype = ci
     L.attn_qk_rmsnorm.argtypes = [vp] * 6 + [ci] * 5 + [cf, ci, vp]
+    L.attn_qk_rmsnorm_split.restype = ci
+    L.attn_qk_rmsnorm_split.argtypes = [vp] * 5 + [ci] * 5 + [cf, ci, vp]
+    L.attn_fwd_qnorm.restype = ci
+    L.attn_fwd_qnorm.argtypes = [vp] * 7 + [ci] * 6 + [cf, ci, vp]
     if path == LIB_PATH:
         _lib = L
     return L
@@ -160,6 +164,36 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     rc = load_library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  lse.data_ptr() if lse is not None else None, B, H, S_q, S_k, d,
                                  int(bool(causal)), float(scale), dt, _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def fwd_qnorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rstd: torch.Tensor, w_q: torch.Tensor,
+              causal: bool = False, scale: float | None = None, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None, want_lse: bool = True):
+    """fwd of RMSNorm(q) with k and v, the norm folded into the kernel's Q loads: q raw, q_rstd
+    [B, S_q] fp32 from qk_rmsnorm_split, w_q [H*d] in q's dtype, k already normalised.  The same
+    bits as fwd(qk_rmsnorm(q, k, w_q, w_k)[0], k_norm, v).  bf16 / fp16 only."""
+    B, H, S_q, S_k, d = _shapes(q, k, v)
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    dt = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _check_buffer(q_rstd, "q_rstd", (B, S_q), torch.float32, q.device)
+    _check_buffer(w_q, "w_q", (H * d,), q.dtype, q.device)
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    _check_buffer(out, "out", (B, H, S_q, d), q.dtype, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_buffer(lse, "lse", (B, H, S_q), torch.float32, q.device)
+    rc = load_library().attn_fwd_qnorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_rstd.data_ptr(), w_q.data_ptr(),
+                                       out.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, S_q,
+                                       S_k, d, int(bool(causal)), float(scale), dt, _stream(q.device))
     _check(rc)
     return out, lse
 
@@ -291,3 +325,29 @@ def qk_rmsnorm(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.T
                                         k_out.data_ptr(), B, H, S_q, S_k, d, float(eps), dt, _stream(q.device))
     _check(rc)
     return q_out, k_out
+
+
+def qk_rmsnorm_split(q: torch.Tensor, k: torch.Tensor, w_k: torch.Tensor, eps: float = 1e-6,
+                     q_rstd: torch.Tensor | None = None, k_out: torch.Tensor | None = None, inplace: bool = False):
+    """K normalised as qk_rmsnorm does it; for Q only the per-token factor r [B, S_q] (fp32), which
+    fwd_qnorm folds into its Q loads.  Returns (q_rstd, k_norm); with inplace=True k_norm is k."""
+    B, H, S_q, S_k, d = _shapes(q, k, k)
+    for t in (q, k, w_k):
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, w_k must be contiguous device tensors of one dtype")
+    if w_k.numel() != H * d:
+        raise ValueError("w_k must have H*d entries")
+    dt = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q_rstd is None:
+        q_rstd = torch.empty((B, S_q), dtype=torch.float32, device=q.device)
+    _check_buffer(q_rstd, "q_rstd", (B, S_q), torch.float32, q.device)
+    if inplace:
+        k_out = k
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _check_buffer(k_out, "k_out", tuple(k.shape), k.dtype, k.device)
+    rc = load_library().attn_qk_rmsnorm_split(q.data_ptr(), k.data_ptr(), w_k.data_ptr(), q_rstd.data_ptr(),
+                                              k_out.data_ptr(), B, H, S_q, S_k, d, float(eps), dt, _stream(q.device))
+    _check(rc)
+    return q_rstd, k_out

@@ -85,6 +85,18 @@ template <> __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// The two 16-bit values of type T in one dword -> floats (low half first).
+template <class T> __device__ __forceinline__ void unpack2(uint32_t u, float &a, float &b);
+template <> __device__ __forceinline__ void unpack2<BF16>(uint32_t u, float &a, float &b) {
+    a = __uint_as_float(u << 16);
+    b = __uint_as_float(u & 0xFFFF0000u);
+}
+template <> __device__ __forceinline__ void unpack2<F16>(uint32_t u, float &a, float &b) {
+    const f16x2 h = __builtin_bit_cast(f16x2, u);
+    a = (float)h[0];
+    b = (float)h[1];
+}
+
 // acc + a.lo + a.hi for a dword holding two 16-bit values of type T (one v_dot2 against ones).
 template <class T> __device__ __forceinline__ float sum2(uint32_t a, float acc);
 template <> __device__ __forceinline__ float sum2<BF16>(uint32_t a, float acc) {
@@ -128,7 +140,35 @@ struct Params {
     int xcd_remap;   // XCD count nx: map workgroups so each XCD gets a contiguous range of heads; 0: off
     float c;         // scale * log2(e)
     int pair;        // causal, classic schedule: a workgroup takes query tiles nqt-1-j and j (see there)
+    // RMSNorm of Q folded into the Q operand loads (null qr: q is used as it is): qr [B][S_q] the
+    // per-token factor, wq [H*d] the per-channel weight
+    const float *qr;
+    const uint16_t *wq;
+    int H;
 };
+
+// One Q^T operand: the 8 values of query row `row`, channels 16 ks + 8 half .. + 7, of head bh.
+// With p.qr set they are RMSNorm(q) as the QKNorm-across-heads step forms it (the sglang write-up,
+// blog.secrett2633): q * r[b][row] * w_q[h*d + channel] in fp32, rounded to nearest even in T, the
+// same operations in the same order as attn_qk_rmsnorm, so the operand is bit for bit the one that
+// attn_qk_rmsnorm would have stored.
+template <class T, int D>
+__device__ __forceinline__ u32x4 load_q_frag(const Params &p, const uint16_t *Qh, int bh, int row, int ks, int half) {
+    u32x4 v = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + half * 8);
+    if (p.qr) {
+        const int b = bh / p.H, h = bh - b * p.H;
+        const float r = p.qr[(size_t)b * p.Sq + row];
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(p.wq + (size_t)h * D + ks * 16 + half * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float a, c, wa, wc;
+            unpack2<T>(v[e], a, c);
+            unpack2<T>(w[e], wa, wc);
+            v[e] = pack2<T>(a * r * wa, c * r * wc);
+        }
+    }
+    return v;
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -560,7 +600,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
             const int row = min(qw0 + qb * 32 + (lq & 31), Sq - 1);
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
-                qf[qb][ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + (lq >> 5) * 8);
+                qf[qb][ks] = load_q_frag<T, D>(p, Qh, bh, row, ks, lq >> 5);
         }
     }
 
@@ -775,7 +815,7 @@ __global__ __launch_bounds__(512) void attn_fwd_dp_kernel(Params p) {
     {
         const int row = min(qw0 + l32, Sq - 1);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
+        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = load_q_frag<T, D>(p, Qh, bh, row, ks, g);
     }
     // the Q fragments are the newest loads; draining them here keeps the memory counter free of
     // them inside the key loop.  Both branches pass n_total barriers.
@@ -936,7 +976,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(Params p) {
         const int row = min(qw0 + l32, Sq - 1);   // rows past S_q: computed, never stored
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-            qf[ks] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)row * D + ks * 16 + g * 8);
+            qf[ks] = load_q_frag<T, D>(p, Qh, bh, row, ks, g);
     }
     __builtin_amdgcn_s_waitcnt(0);
     wg_barrier();
@@ -1672,11 +1712,14 @@ constexpr int kShapes[][5] = {
     {ATTN_SCHED_CLASSIC, 1, 8, 3, 64},  {ATTN_SCHED_CLASSIC, 1, 8, 4, 64},  {ATTN_SCHED_CLASSIC, 2, 4, 3, 64},
     {ATTN_SCHED_CLASSIC, 2, 4, 4, 64},  {ATTN_SCHED_CLASSIC, 1, 4, 2, 64},  {ATTN_SCHED_CLASSIC, 1, 4, 3, 64},
     {ATTN_SCHED_CLASSIC, 2, 8, 3, 64},  {ATTN_SCHED_CLASSIC, 2, 8, 4, 64},  {ATTN_SCHED_CLASSIC, 1, 8, 2, 128},
-    {ATTN_SCHED_PINGPONG, 1, 8, 3, 64}, {ATTN_SCHED_DEPHASED, 1, 8, 4, 64}};
+    {ATTN_SCHED_CLASSIC, 1, 4, 3, 192}, {ATTN_SCHED_CLASSIC, 1, 4, 2, 256}, {ATTN_SCHED_PINGPONG, 1, 8, 3, 64},
+    {ATTN_SCHED_DEPHASED, 1, 8, 4, 64}};
 // (2, 8, *) holds 64 queries per wave at two waves per SIMD, which fits the registers at d = 64
 // only; at d = 128 plans and launches with it return ATTN_ERR_UNSUPPORTED.  128-key tiles take
-// 64 KiB of LDS per stage at d = 128, so two stages; 192 or more keys per tile would not fit two
-// waves' registers per SIMD.
+// 64 KiB of LDS per stage at d = 128, so two stages.  192 and 256 keys per tile (d = 64 only, the
+// same error at d = 128, where one stage would take 96 or 128 KiB) run one wave per SIMD: their
+// scores alone take 96 or 128 registers a lane, which two waves per SIMD cannot hold (they
+// spill 172-396 bytes a lane there); one wave has the matrix-core registers of the SIMD to itself.
 
 bool compiled_shape(int sched, int qb, int nw, int ns, int bk) {
     for (const auto &sh : kShapes)
@@ -1708,11 +1751,13 @@ int policy_override() {
 // Tile policy, measured on MI355X (bf16 B=2 H=16 S=4096, B=4 H=16 S=2048 and causal B=1 H=32
 // S=8192 at d=128; causal B=1 H=16 S=16384 and B=1 H=2 S=128 at d=64).  d=128: the classic
 // schedule with 128-key tiles and two stages is 1.4-2.1% faster than the de-phased schedule on
-// 64-key tiles, which in turn is 1.5-2% faster than the classic schedule on 64-key tiles.  d=64:
-// the classic schedule with 64 queries per wave (2, 8, 4) is 7% faster than with 32 (1, 8, 4) as
+// 64-key tiles, which in turn is 1.5-2% faster than the classic schedule on 64-key tiles (causal
+// S=8192 with paired tiles: 495 us against 524 for (1, 8, 4, 64) and 564 de-phased).  d=64: the
+// classic schedule with 64 queries per wave (2, 8, 4) is 7% faster than with 32 (1, 8, 4) as
 // long as its 512-query workgroups fill the 256 CUs (slower on the tiny S=128 workload, which
-// they do not), except causal, where 128-key tiles (1, 8, 2) are 1.5% faster again; the
-// de-phased schedule is not faster there.  Choosing the kernel variant at run time from a table
+// they do not), causal too now that causal tiles go in pairs (B=1 H=16 S=16384: 586 against
+// 606 us for (1, 8, 2, 128), which had been 1.5% faster unpaired); the de-phased schedule is not
+// faster there, nor are 192- or 256-key tiles (one wave per SIMD: 27-38% slower).  Choosing the kernel variant at run time from a table
 // measured per shape and keyed on the device's compute-unit count is the runtime policy of the
 // FlashInfer KDA write-up (blog.secrett2633), its section 1 and its closing lessons.
 void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
@@ -1725,16 +1770,7 @@ void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
     } else {
         pl->ns = 4;
         pl->bk = 64;
-        if ((long long)B * H * ((Sq + 511) / 512) >= device_info().cus) {
-            pl->qb = 2;
-            // causal at that size: 128-key tiles with 32 queries per wave are 1.5% faster still
-            // (B=1 H=16 S=16384: 627.0 vs 636.7 us); non-causal they are 1.7% slower
-            if (causal) {
-                pl->qb = 1;
-                pl->ns = 2;
-                pl->bk = 128;
-            }
-        }
+        if ((long long)B * H * ((Sq + 511) / 512) >= device_info().cus) pl->qb = 2;
     }
     // at most 128 query rows: 256-query workgroups would compute as many clamped rows as real
     // ones; 4 waves of 32 queries compute none (B=1 H=2 S=128 d=64: 7.4 vs 7.8 us per launch)
@@ -1757,6 +1793,7 @@ void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
 int make_plan(int B, int H, int Sq, int d, int causal, Plan *pl) {
     choose_policy(B, H, Sq, d, causal, pl);
     if (pl->qb == 2 && pl->nw == 8 && d != 64) return ATTN_ERR_UNSUPPORTED;   // registers: d = 64 only
+    if (pl->bk > 128 && d != 64) return ATTN_ERR_UNSUPPORTED;                 // LDS: d = 64 only
     pl->block_q = pl->nw * pl->qb * 32;
     pl->block_k = pl->bk;
     pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
@@ -1789,6 +1826,15 @@ int launch_shape(const Params &p, const Plan &pl, hipStream_t s) {
     }
     if (pl.bk == 128) {
         if (pl.qb == 1 && pl.nw == 8 && pl.ns == 2) return launch<T, D, CAUSAL, 1, 8, 2, 128>(p, pl, s);
+        return ATTN_ERR_UNSUPPORTED;
+    }
+    if (pl.bk == 192 || pl.bk == 256) {
+        if constexpr (D == 64) {
+            if (pl.bk == 192 && pl.qb == 1 && pl.nw == 4 && pl.ns == 3)
+                return launch<T, D, CAUSAL, 1, 4, 3, 192>(p, pl, s);
+            if (pl.bk == 256 && pl.qb == 1 && pl.nw == 4 && pl.ns == 2)
+                return launch<T, D, CAUSAL, 1, 4, 2, 256>(p, pl, s);
+        }
         return ATTN_ERR_UNSUPPORTED;
     }
     const int key = pl.qb * 100 + pl.nw * 10 + pl.ns;
@@ -1882,20 +1928,11 @@ int check_descales(const float *q_descale, const float *k_descale, const float *
     return ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S_q,
-                        int S_k, int d, int causal, float scale, int dtype, void *stream) {
-    if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3 && dtype != ATTN_FP8_E5M2)
-        return ATTN_ERR_UNSUPPORTED;
-    int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
-    if (st == kEmpty) return ATTN_OK;
-    if (st != ATTN_OK) return st;
-    if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2)
-        return run_fp8(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, S_q, S_k, d, causal, scale,
-                       dtype == ATTN_FP8_E5M2 ? 1 : 0, stream);
+// f16 / bf16 attention (arguments checked); q_rstd and w_q non-null fold RMSNorm into Q
+int run_half(const void *q, const void *k, const void *v, const float *q_rstd, const void *w_q, void *o, float *lse,
+             int B, int H, int S_q, int S_k, int d, int causal, float scale, int dtype, void *stream) {
     Plan pl;
-    st = make_plan(B, H, S_q, d, causal, &pl);
+    int st = make_plan(B, H, S_q, d, causal, &pl);
     if (st != ATTN_OK) return st;
     Params p;
     p.q = static_cast<const uint16_t *>(q);
@@ -1910,9 +1947,40 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     p.xcd_remap = xcd_remap_for(pl.num_wg);
     p.c = scale * 1.44269504088896340736f;
     p.pair = pl.pair;
+    p.qr = q_rstd;
+    p.wq = static_cast<const uint16_t *>(w_q);
+    p.H = H;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == ATTN_BF16) return dispatch<BF16>(p, pl, d, causal, s);
     return dispatch<F16>(p, pl, d, causal, s);
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int S_q,
+                        int S_k, int d, int causal, float scale, int dtype, void *stream) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3 && dtype != ATTN_FP8_E5M2)
+        return ATTN_ERR_UNSUPPORTED;
+    int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
+    if (st == kEmpty) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    if (dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2)
+        return run_fp8(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, S_q, S_k, d, causal, scale,
+                       dtype == ATTN_FP8_E5M2 ? 1 : 0, stream);
+    return run_half(q, k, v, nullptr, nullptr, o, lse, B, H, S_q, S_k, d, causal, scale, dtype, stream);
+}
+
+extern "C" int attn_fwd_qnorm(const void *q, const void *k, const void *v, const float *q_rstd, const void *w_q,
+                              void *o, float *lse, int B, int H, int S_q, int S_k, int d, int causal, float scale,
+                              int dtype, void *stream) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    int st = check_common(q, k, v, o, lse, B, H, S_q, S_k, d, scale);
+    if (st == kEmpty) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    if (!q_rstd || !w_q) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(q_rstd) & 3u) || (reinterpret_cast<uintptr_t>(w_q) & 15u)) return ATTN_ERR_ALIGN;
+    if ((long long)B * S_q > INT_MAX || (long long)H * d > INT_MAX) return ATTN_ERR_OVERFLOW;
+    return run_half(q, k, v, q_rstd, w_q, o, lse, B, H, S_q, S_k, d, causal, scale, dtype, stream);
 }
 
 extern "C" int attn_fwd_fp8(const void *q, const void *k, const void *v, const float *q_descale,

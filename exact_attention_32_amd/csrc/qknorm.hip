@@ -12,6 +12,11 @@
 // 16 l' .. 16 l' + 15 (d = 128) read one 256-byte row, and one wave load covers 4 heads (8 at
 // d = 64).  Holding the token in registers makes the in-place call safe: every value of a token
 // is read before any is written.
+//
+// The split form (attn_qk_rmsnorm_split) normalises K the same way but writes, for Q, only the
+// factor r of each token (4 bytes instead of the 2 H d bytes of the normalised row); attention
+// then applies q * r * w_q to its Q operands as it loads them (attn_fwd_qnorm), with the same
+// arithmetic, so the result is the same bits as normalising Q here first.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -68,6 +73,7 @@ struct QnParams {
     int S[2];
     int B, H;
     float eps;
+    float *rstd;   // non-null: Q's factor r per token goes here instead of the normalised Q
 };
 
 template <class T, int D, int NG>
@@ -106,6 +112,10 @@ __global__ __launch_bounds__(QN_WAVES * 64) void qk_rmsnorm_kernel(QnParams p) {
     }
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(p.eps + ss / (float)(H * D));
+    if (which == 0 && p.rstd) {
+        if (lane == 0) p.rstd[tok] = r;   // tok = b * S + s
+        return;
+    }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         const int h = gi * HPL + hsub;
@@ -149,9 +159,11 @@ int launch_qn(const QnParams &p, int d, int nwg, hipStream_t s) {
 
 }  // namespace
 
-extern "C" int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, const void *w_k, void *q_out,
-                               void *k_out, int B, int H, int S_q, int S_k, int d, float eps, int dtype,
-                               void *stream) {
+namespace {
+
+// split false: Q and K normalised; true: K normalised and Q's factor r written to q_rstd
+int run_qn(const void *q, const void *k, const void *w_q, const void *w_k, void *q_out, void *k_out, float *q_rstd,
+           bool split, int B, int H, int S_q, int S_k, int d, float eps, int dtype, void *stream) {
     if (B < 0 || H < 0 || S_q < 0 || S_k < 0) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
     if (dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
@@ -159,12 +171,12 @@ extern "C" int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, co
     if (!std::isfinite(eps) || eps < 0.f) return ATTN_ERR_VALUE;
     if (B == 0 || H == 0 || (S_q == 0 && S_k == 0)) return ATTN_OK;   // no tokens: nothing to do
     // a tensor with no tokens is not read or written: its pointers may be NULL
-    if (S_q > 0 && (!q || !w_q || !q_out)) return ATTN_ERR_NULL;
+    if (S_q > 0 && (!q || (split ? !q_rstd : (!w_q || !q_out)))) return ATTN_ERR_NULL;
     if (S_k > 0 && (!k || !w_k || !k_out)) return ATTN_ERR_NULL;
     const uintptr_t mis = (reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                            reinterpret_cast<uintptr_t>(w_q) | reinterpret_cast<uintptr_t>(w_k) |
                            reinterpret_cast<uintptr_t>(q_out) | reinterpret_cast<uintptr_t>(k_out)) & 15u;
-    if (mis) return ATTN_ERR_ALIGN;
+    if (mis || (reinterpret_cast<uintptr_t>(q_rstd) & 3u)) return ATTN_ERR_ALIGN;
     const long long tq = (long long)B * S_q, tk = (long long)B * S_k;
     const long long tmax = tq > tk ? tq : tk;
     if (tmax > INT_MAX || (long long)B * H > INT_MAX || (long long)S_q * d > INT_MAX || (long long)S_k * d > INT_MAX)
@@ -182,6 +194,20 @@ extern "C" int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, co
     p.B = B;
     p.H = H;
     p.eps = eps;
+    p.rstd = q_rstd;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dtype == ATTN_BF16 ? launch_qn<Bf16>(p, d, (int)nwg, s) : launch_qn<F16>(p, d, (int)nwg, s);
+}
+
+}  // namespace
+
+extern "C" int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, const void *w_k, void *q_out,
+                               void *k_out, int B, int H, int S_q, int S_k, int d, float eps, int dtype,
+                               void *stream) {
+    return run_qn(q, k, w_q, w_k, q_out, k_out, nullptr, false, B, H, S_q, S_k, d, eps, dtype, stream);
+}
+
+extern "C" int attn_qk_rmsnorm_split(const void *q, const void *k, const void *w_k, float *q_rstd, void *k_out,
+                                     int B, int H, int S_q, int S_k, int d, float eps, int dtype, void *stream) {
+    return run_qn(q, k, nullptr, w_k, nullptr, k_out, q_rstd, true, B, H, S_q, S_k, d, eps, dtype, stream);
 }

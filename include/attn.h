@@ -75,6 +75,23 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
              int d, int causal, float scale, int dtype, void *stream);
 
 /*
+ * attn_fwd of RMSNorm(q) with k and v, the RMSNorm folded into the loads of
+ * the Q operands (the QKNorm-across-heads write-up's norm, Q side): every Q
+ * value the kernel uses is q[b,h,s,t] * q_rstd[b*S_q + s] * w_q[h*d + t],
+ * computed in fp32 and rounded to nearest even in dtype, which is bit for bit
+ * what attn_qk_rmsnorm stores, so O and LSE are those of attn_fwd on
+ * attn_qk_rmsnorm's output.  q: the raw queries; q_rstd: [B][S_q] floats from
+ * attn_qk_rmsnorm_split (4-byte aligned); w_q: [H*d] weights in dtype
+ * (16-byte aligned); k: normalised keys (attn_qk_rmsnorm_split's k_out).
+ * dtype: ATTN_BF16 or ATTN_F16 only (else ATTN_ERR_UNSUPPORTED); other
+ * arguments, checks and the empty cases as attn_fwd; ATTN_ERR_NULL when q_rstd
+ * or w_q is NULL with work to do.  Returns an attn_status.
+ */
+int attn_fwd_qnorm(const void *q, const void *k, const void *v, const float *q_rstd, const void *w_q, void *o,
+                   float *lse, int B, int H, int S_q, int S_k, int d, int causal, float scale, int dtype,
+                   void *stream);
+
+/*
  * Exact-attention forward for block-scaled fp8 inputs (the FlashAttention-3
  * deep dive, section 4: per-block scale factors from each block's local
  * maximum; the score product in FP8, the softmax and the output accumulated
@@ -162,6 +179,20 @@ int attn_qk_rmsnorm(const void *q, const void *k, const void *w_q, const void *w
                     int B, int H, int S_q, int S_k, int d, float eps, int dtype, void *stream);
 
 /*
+ * The same step with Q's normalisation left to attention (the fused prologue
+ * of the QKNorm-across-heads write-up, Q side): K is normalised exactly as
+ * attn_qk_rmsnorm does it (k_out, in place allowed); for Q only the per-token
+ * factor is written,
+ *   q_rstd[b*S_q + s] = rsqrt(eps + sum_{h,t} q[b,h,s,t]^2 / (H*d))   (fp32),
+ * the same value attn_qk_rmsnorm multiplies by.  q_rstd: device pointer,
+ * [B][S_q] floats, 4-byte aligned; w_q is not needed here (attn_fwd_qnorm
+ * takes it).  Other arguments, checks and the empty cases as
+ * attn_qk_rmsnorm; q_rstd may be NULL when S_q = 0.  Returns an attn_status.
+ */
+int attn_qk_rmsnorm_split(const void *q, const void *k, const void *w_k, float *q_rstd, void *k_out, int B, int H,
+                          int S_q, int S_k, int d, float eps, int dtype, void *stream);
+
+/*
  * Tile policy.  attn_fwd picks a compiled kernel variant (schedule and tile shape) at run time from
  * a table measured on MI355X, keyed on the shape (d, causal, dtype, S_q, B*H) and on the device's
  * compute-unit count, the runtime policy that the FlashInfer KDA write-up (blog.secrett2633)
@@ -184,7 +215,8 @@ typedef enum {
  * the measured policy table.  Compiled, as (qb, nw, ns, bk):
  *   CLASSIC   (1,8,3,64) (1,8,4,64) (2,4,3,64) (2,4,4,64) (1,4,2,64)
  *             (1,4,3,64) (1,8,2,128), and for d = 64 only (2,8,3,64)
- *             (2,8,4,64) (attn_fwd returns ATTN_ERR_UNSUPPORTED at d = 128);
+ *             (2,8,4,64) (1,4,3,192) (1,4,2,256) (attn_fwd returns
+ *             ATTN_ERR_UNSUPPORTED for these at d = 128);
  *   PINGPONG  (1,8,3,64);  DEPHASED (1,8,4,64).
  * schedule = ATTN_SCHED_DEFAULT restores the table (the other arguments are
  * then ignored).  The environment variable ATTN_FWD_POLICY =

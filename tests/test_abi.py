@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"attn_fwd", "attn_fwd_fp8", "attn_fwd_fp8_e5m2", "attn_status_string", "attn_fwd_plan",
                           "attn_quantize_e4m3", "attn_quantize_e5m2", "attn_fwd_set_policy", "attn_qk_rmsnorm",
-                          "attn_quantize_qkv"}
+                          "attn_quantize_qkv", "attn_qk_rmsnorm_split", "attn_fwd_qnorm"}
     for n in names:
         assert hasattr(lib, n), f"library does not export {n}"
 
@@ -176,7 +176,7 @@ def test_quantize_validation(lib):
 C, PP, DP = ea.ATTN_SCHED_CLASSIC, ea.ATTN_SCHED_PINGPONG, ea.ATTN_SCHED_DEPHASED
 COMPILED = [(C, 1, 8, 3, 64), (C, 1, 8, 4, 64), (C, 2, 4, 3, 64), (C, 2, 4, 4, 64), (C, 1, 4, 2, 64),
             (C, 1, 4, 3, 64), (C, 1, 8, 2, 128), (PP, 1, 8, 3, 64), (DP, 1, 8, 4, 64)]
-D64_ONLY = [(C, 2, 8, 3, 64), (C, 2, 8, 4, 64)]
+D64_ONLY = [(C, 2, 8, 3, 64), (C, 2, 8, 4, 64), (C, 1, 4, 3, 192), (C, 1, 4, 2, 256)]
 
 
 def test_set_policy(lib):
@@ -192,7 +192,7 @@ def test_set_policy(lib):
             assert ea.plan(2, 16, 4096, 4096, 128, False, dtype=ea.ATTN_FP8_E4M3)[:3] == (256, 128, 8)
         for sched, qb, nw, ns, bkk in D64_ONLY:
             assert lib.attn_fwd_set_policy(sched, qb, nw, ns, bkk) == OK
-            assert ea.plan(1, 16, 4096, 4096, 64, False)[:3] == (512, 64, 8)
+            assert ea.plan(1, 16, 4096, 4096, 64, False)[:3] == (qb * nw * 32, bkk, nw)
             with pytest.raises(ea.AttnError):
                 ea.plan(1, 16, 4096, 4096, 128, False)
     finally:
@@ -200,10 +200,9 @@ def test_set_policy(lib):
     # the measured table: d = 128 takes 128-key tiles
     assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 128, 8)
     assert ea.kernel_name(128, False, ea.ATTN_BF16) == "attn_fwd_kernel"
-    # d = 64: 64 queries per wave once the 512-query workgroups fill the 256 CUs; causal at that
-    # size, 128-key tiles with 32 queries per wave
+    # d = 64: 64 queries per wave once the 512-query workgroups fill the 256 CUs, causal or not
     assert ea.plan(1, 16, 16384, 16384, 64, False)[:3] == (512, 64, 8)
-    assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (256, 128, 8)
+    assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (512, 64, 8)
     # at most 128 query rows: 128-query workgroups (no clamped rows computed)
     assert ea.plan(1, 2, 128, 128, 64, False)[:3] == (128, 64, 4)
     assert ea.plan(1, 2, 129, 128, 64, False)[:3] == (256, 64, 8)
@@ -214,7 +213,7 @@ def test_plan_causal_pairs(lib):
     query tiles (n-1-j, j); smaller ones, non-causal ones and fp8 one per tile.  (Here, without a
     device, the CU count is the 256 the table was measured on.)"""
     assert ea.plan(1, 32, 8192, 8192, 128, True) == (256, 128, 8, 32 * 16)
-    assert ea.plan(1, 16, 16384, 16384, 64, True) == (256, 128, 8, 16 * 32)
+    assert ea.plan(1, 16, 16384, 16384, 64, True) == (512, 64, 8, 16 * 16)
     assert ea.plan(2, 43, 1200, 1200, 128, True)[3] == 2 * 43 * 3   # 5 tiles: 2 pairs and 1 alone
     assert ea.plan(1, 32, 8192, 8192, 128, False)[3] == 32 * 32
     assert ea.plan(1, 2, 1024, 1024, 128, True)[3] == 2 * 4   # 4 pairs would leave CUs idle
@@ -238,6 +237,45 @@ def test_qk_rmsnorm_validation(lib):
     for e in (-1e-6, float("nan"), float("inf")):
         assert callqn(lib, eps=e) == VALUE
     assert callqn(lib, B=2 ** 16, Sq=2 ** 16) == OVERFLOW
+
+
+def callqs(lib, q=P, k=P, wk=P, r=P, ko=P, B=1, H=2, Sq=16, Sk=16, d=128, eps=1e-6, dtype=1):
+    return lib.attn_qk_rmsnorm_split(q, k, wk, r, ko, B, H, Sq, Sk, d, eps, dtype, None)
+
+
+def test_qk_rmsnorm_split_validation(lib):
+    for kw in ("q", "k", "wk", "r", "ko"):
+        assert callqs(lib, **{kw: None}) == NULL
+    for kw in ("q", "k", "wk", "ko"):
+        assert callqs(lib, **{kw: P + 8}) == ALIGN
+    assert callqs(lib, r=P + 2) == ALIGN   # the factors are floats: 4-byte alignment
+    for kw in ("B", "H", "Sq", "Sk"):
+        assert callqs(lib, **{kw: -1}) == SHAPE
+    assert callqs(lib, Sq=0, r=None, k=None) == NULL and callqs(lib, Sk=0, q=P, r=None) == NULL
+    assert callqs(lib, d=96) == UNSUP and callqs(lib, dtype=2) == UNSUP
+    assert callqs(lib, eps=float("nan")) == VALUE
+    assert callqs(lib, B=0) == OK and callqs(lib, Sq=0, Sk=0) == OK
+
+
+def callfq(lib, q=P, k=P, v=P, r=P, wq=P, o=P, lse=P, B=1, H=2, Sq=16, Sk=16, d=128, causal=0, scale=0.125, dtype=1):
+    return lib.attn_fwd_qnorm(q, k, v, r, wq, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, None)
+
+
+def test_fwd_qnorm_validation(lib):
+    for kw in ("q", "k", "v", "o", "r", "wq"):
+        assert callfq(lib, **{kw: None}) == NULL
+    for kw in ("q", "k", "v", "o", "wq"):
+        assert callfq(lib, **{kw: P + 8}) == ALIGN
+    assert callfq(lib, r=P + 2) == ALIGN and callfq(lib, lse=P + 2) == ALIGN
+    for kw in ("B", "H", "Sq", "Sk"):
+        assert callfq(lib, **{kw: -1}) == SHAPE
+    assert callfq(lib, Sk=0) == SHAPE
+    for dt in (0, 1):
+        assert callfq(lib, d=96, dtype=dt) == UNSUP
+    assert callfq(lib, dtype=2) == UNSUP and callfq(lib, dtype=4) == UNSUP and callfq(lib, dtype=3) == UNSUP
+    assert callfq(lib, scale=float("inf")) == VALUE
+    # no query rows: nothing to do, and the factor and weight pointers are not needed
+    assert callfq(lib, Sq=0, r=None, wq=None) == OK and callfq(lib, B=0) == OK
 
 
 def callqkv(lib, q=P, k=P, v=P, dtype=3, fmt=2, cq=P, ck=P, cv=P, dq=P, dk=P, dv=P, B=1, H=1, Sq=16, Sk=16, d=128):

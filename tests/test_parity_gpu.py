@@ -86,8 +86,8 @@ def test_small_full_e5m2(oracle, shape, causal):
 
 SCHEDULES = [(1, 1, 8, 3, 64), (1, 1, 8, 4, 64), (1, 2, 4, 3, 64), (1, 2, 4, 4, 64), (1, 1, 4, 2, 64),
              (1, 1, 4, 3, 64), (1, 1, 8, 2, 128), (2, 1, 8, 3, 64), (3, 1, 8, 4, 64), (1, 2, 8, 3, 64),
-             (1, 2, 8, 4, 64)]
-D64_ONLY = {(1, 2, 8, 3, 64), (1, 2, 8, 4, 64)}
+             (1, 2, 8, 4, 64), (1, 1, 4, 3, 192), (1, 1, 4, 2, 256)]
+D64_ONLY = {(1, 2, 8, 3, 64), (1, 2, 8, 4, 64), (1, 1, 4, 3, 192), (1, 1, 4, 2, 256)}
 SCHED_SHAPES = [(1, 1, 1, 1, 64), (1, 2, 17, 3, 128), (2, 3, 130, 130, 64), (1, 2, 300, 333, 128),
                 (1, 2, 513, 257, 128), (1, 2, 1000, 1000, 64)]
 
@@ -118,7 +118,7 @@ def test_every_schedule(oracle, sched):
 # causal shapes whose (batch, head) count makes the library pair query tiles (n-1-j, j) in one
 # workgroup, the light tile with its keys in reverse order: even and odd tile counts (an odd one
 # leaves the middle tile alone), S_q < S_k and S_q > S_k, both head dimensions and tile shapes
-PAIRED = [(1, 128, 1024, 1024, 64), (2, 43, 1200, 1200, 128), (1, 128, 1000, 1100, 128), (1, 100, 1300, 900, 64)]
+PAIRED = [(1, 128, 2048, 2048, 64), (2, 43, 1200, 1200, 128), (1, 128, 1000, 1100, 128), (2, 100, 1300, 900, 64)]
 
 
 @pytest.mark.parametrize("shape", PAIRED, ids=lambda s: "x".join(map(str, s)))
@@ -142,9 +142,10 @@ def test_causal_pairs_rising(oracle, kind):
     import exact_attention_32_amd as ea
 
     dev = "cuda:0"
-    for d, dtype in ((64, "bf16"), (128, "f16")):
-        q, k, v = _rising_inputs(kind, 1, 128, 1024, d, dtype, seed=d + 11)
-        assert ea.plan(1, 128, 1024, 1024, d, True)[3] == 128 * 2
+    for d, dtype, S in ((64, "bf16", 2048), (128, "f16", 1024)):
+        q, k, v = _rising_inputs(kind, 1, 128, S, d, dtype, seed=d + 11)
+        bq, _, _, n = ea.plan(1, 128, S, S, d, True)
+        assert S // bq == 4 and n == 128 * 2   # four query tiles a head, in two pairs
         U.say(f"[gpu] pairs rising {kind} d={d} {dtype}")
         o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=True, scale=d ** -0.5)
         torch.cuda.synchronize()

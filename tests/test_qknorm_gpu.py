@@ -114,6 +114,92 @@ def test_qknorm_then_attention(oracle, shape, causal):
     assert st["pass"], st
 
 
+FOLD = [(1, 4, 300, 333, 128, False), (2, 8, 257, 257, 64, True), (1, 16, 1000, 1000, 128, True),
+        (1, 128, 2048, 2048, 64, True), (2, 64, 1024, 1024, 128, True), (2, 3, 17, 5, 64, False)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", FOLD, ids=lambda s: "x".join(map(str, s)))
+def test_qnorm_fold_equals_separate(oracle, shape, dtype):
+    """Q's RMSNorm folded into attention's Q loads: K and the attention output are bit for bit those
+    of the separate norm followed by attention, and the per-token factor is the norm's."""
+    import exact_attention_32_amd as ea
+
+    B, H, Sq, Sk, d, causal = shape
+    dev = "cuda:0"
+    q, wq = _draw(B, H, Sq, d, dtype, 70 + Sq)
+    k, wk = _draw(B, H, Sk, d, dtype, 80 + Sk)
+    v = torch.randn(B, H, Sk, d, generator=torch.Generator().manual_seed(90)).to(TDT[dtype])
+    q, k, v, wq, wk = q.to(dev), k.to(dev), v.to(dev), wq.to(dev), wk.to(dev)
+    eps = 1e-6
+    U.say(f"[gpu] qnorm fold {shape} {dtype}")
+    qn, kn = ea.qk_rmsnorm(q, k, wq, wk, eps=eps)
+    o1, l1 = ea.fwd(qn, kn, v, causal=causal)
+    r, kn2 = ea.qk_rmsnorm_split(q, k, wk, eps=eps)
+    o2, l2 = ea.fwd_qnorm(q, kn2, v, r, wq, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(kn, kn2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # the factor against the oracle's norm: q * r * w reproduces the fp64 RMSNorm to fp32 accuracy
+    ref = oracle.rmsnorm_across_heads(q.double().cpu().numpy(), wq.double().cpu().numpy(), eps)
+    recon = (q.double().cpu() * r.double().cpu()[:, None, :, None] * wq.double().cpu().view(H, 1, d)).numpy()
+    err = np.abs(recon - ref) / np.maximum(np.abs(ref), 1e-30)
+    # (fp32 sums over up to H*d = 8192 squares: a few parts in 10^6 at most)
+    assert float(err[np.abs(ref) > 0].max(initial=0.0)) < 2e-5
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 4, 300, 333, 128), (2, 8, 257, 257, 64)], ids=lambda s: "x".join(map(str, s)))
+def test_qnorm_fold_oracle(oracle, shape, causal):
+    """Folded norm -> attention against RMSNorm (fp64, rounded to bf16) then attention (fp64), at the
+    shapes of the separate path's oracle test.  (The reference rounds the fp64 norm, the kernel an
+    fp32 one, so a few normalised values sit one bf16 ulp apart; through a large score one such
+    value moves a row's LSE by up to ~1e-2, and at large hidden sizes (H*d = 8192) some row meets
+    one.  The pairing shapes are covered by bit equality with the separate path above.)"""
+    import exact_attention_32_amd as ea
+
+    B, H, Sq, Sk, d = shape
+    dev = "cuda:0"
+    q, wq = _draw(B, H, Sq, d, "bf16", 40 + Sq)   # the separate path's test draws
+    k, wk = _draw(B, H, Sk, d, "bf16", 50 + Sk)
+    v = torch.randn(B, H, Sk, d, generator=torch.Generator().manual_seed(60)).to(torch.bfloat16)
+    eps, scale = 1e-6, d ** -0.5
+    U.say(f"[gpu] qnorm fold vs oracle {shape} causal={causal}")
+    r, kn = ea.qk_rmsnorm_split(q.to(dev), k.to(dev), wk.to(dev), eps=eps)
+    o, lse = ea.fwd_qnorm(q.to(dev), kn, v.to(dev), r, wq.to(dev), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    qr = torch.from_numpy(oracle.rmsnorm_across_heads(q.double().numpy(), wq.double().numpy(), eps)).to(torch.bfloat16)
+    kr = torch.from_numpy(oracle.rmsnorm_across_heads(k.double().numpy(), wk.double().numpy(), eps)).to(torch.bfloat16)
+    ro, rl = oracle.attention(qr.double().numpy(), kr.double().numpy(), v.double().numpy(), causal, scale)
+    st = U.compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "bf16")
+    U.say(f"   {st}")
+    assert st["pass"], st
+
+
+def test_qnorm_fold_every_schedule(oracle):
+    """The fold in every kernel that f16/bf16 attention can launch."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    q, wq = _draw(1, 4, 300, 128, "bf16", 61)
+    k, wk = _draw(1, 4, 333, 128, "bf16", 62)
+    v = torch.randn(1, 4, 333, 128, generator=torch.Generator().manual_seed(63)).to(torch.bfloat16)
+    q, k, v, wq, wk = q.to(dev), k.to(dev), v.to(dev), wq.to(dev), wk.to(dev)
+    qn, kn = ea.qk_rmsnorm(q, k, wq, wk)
+    r, _ = ea.qk_rmsnorm_split(q, k, wk)
+    try:
+        for sched in ((1, 1, 8, 2, 128), (1, 1, 8, 4, 64), (2, 1, 8, 3, 64), (3, 1, 8, 4, 64)):
+            ea.set_policy(*sched)
+            for causal in (False, True):
+                U.say(f"[gpu] qnorm fold sched={sched} causal={causal}")
+                o1, l1 = ea.fwd(qn, kn, v, causal=causal)
+                o2, l2 = ea.fwd_qnorm(q, kn, v, r, wq, causal=causal)
+                torch.cuda.synchronize()
+                assert torch.equal(o1, o2) and torch.equal(l1, l2), (sched, causal)
+    finally:
+        ea.set_policy(ea.ATTN_SCHED_DEFAULT)
+
+
 def test_qknorm_empty(oracle):
     """A tensor with no tokens is not touched; the other one is normalised as usual."""
     import exact_attention_32_amd as ea
