@@ -1861,8 +1861,8 @@ int dispatch(const Params &p, const Plan &pl, int d, int causal, hipStream_t s) 
     return causal ? launch_shape<T, 64, true>(p, pl, s) : launch_shape<T, 64, false>(p, pl, s);
 }
 
-// fp8: 8 waves x 32 queries, 128-key tiles (one descale block), two stages (measured 2-3% faster
-// than three or four on every fp8 workload: B2 H16 S4096 d128 184 vs 189 us, causal S8192 362 vs 371)
+// fp8: 8 waves x 32 queries, 128-key tiles (one descale block), four stages: step t reads the V
+// tile of t-1 (its P.V runs one step late) and the K tile of t while tiles t+1 and t+2 load
 constexpr int kFp8Stages = 4;
 
 void make_plan_fp8(int B, int H, int Sq, Plan *pl) {
