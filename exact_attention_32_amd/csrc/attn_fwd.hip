@@ -28,8 +28,11 @@
 //   * exp2 with log2(e) folded into the scale (the page's section 4 computes the
 //     exponent in base 2); lazy rescaling of O;
 //   * causal: tiles wholly above the diagonal are never loaded; the mask is
-//     applied only on diagonal and tail tiles; query tiles are dispatched
-//     heaviest first and all tiles of one head land on one XCD.
+//     applied only on diagonal and tail tiles; all query tiles of one head land
+//     on one XCD, taken in pairs (n-1-j, j) per workgroup when there are enough
+//     of them (else heaviest first);
+//   * the Q operands can carry the RMSNorm of the QKNorm-across-heads step,
+//     applied as they are loaded (attn_fwd_qnorm).
 //
 // Kernels: attn_fwd_kernel (the schedule above; the policy table's choice at both
 // head dims), attn_fwd_dp_kernel (SIMD partner waves one softmax apart) and
