@@ -374,25 +374,38 @@ def test_empty_queries(oracle):
     assert st["pass"], st
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "qnorm"])
 def test_graph_replay_equals_eager(oracle, dtype):
     """The attention launch captured in a HIP graph (the library allocates nothing and records no
     memset): three replays, with eager work and synchronisations between them, each bit-equal to
-    the eager result."""
+    the eager result.  'qnorm': the split QK-RMSNorm and the attention with the Q fold, two
+    launches in one graph."""
     import exact_attention_32_amd as ea
 
     dev = "cuda:0"
     U.say(f"[gpu] graph replay {dtype}")
-    w = I.random_workload(1, 4, 700, 900, 128, dtype, True, seed=31)
+    w = I.random_workload(1, 4, 700, 900, 128, "bf16" if dtype == "qnorm" else dtype, True, seed=31)
     x = I.make_inputs(w)
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     o = torch.empty((w.B, w.H, w.S_q, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
+    scratch = []   # intermediate tensors the graph must rewrite on every replay
     if dtype == "fp8":
         qd, kd, vd = x.q_descale.to(dev), x.k_descale.to(dev), x.v_descale.to(dev)
 
         def run():
             ea.fwd_fp8(q, k, v, qd, kd, vd, causal=True, scale=w.scale, out=o, lse=lse)
+    elif dtype == "qnorm":
+        g = torch.Generator().manual_seed(32)
+        wq = (torch.rand(w.H * w.d, generator=g) + 0.5).to(torch.bfloat16).to(dev)
+        wk = (torch.rand(w.H * w.d, generator=g) + 0.5).to(torch.bfloat16).to(dev)
+        r = torch.empty((w.B, w.S_q), dtype=torch.float32, device=dev)
+        kn = torch.empty_like(k)
+        scratch = [r, kn]
+
+        def run():
+            ea.qk_rmsnorm_split(q, k, wk, q_rstd=r, k_out=kn)
+            ea.fwd_qnorm(q, kn, v, r, wq, causal=True, scale=w.scale, out=o, lse=lse)
     else:
         def run():
             ea.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
@@ -411,6 +424,8 @@ def test_graph_replay_equals_eager(oracle, dtype):
     for rep in range(3):
         o.fill_(7.0)
         lse.fill_(7.0)
+        for t in scratch:
+            t.fill_(7.0)
         junk = torch.randn(1024, 1024, device=dev) @ torch.randn(1024, 1024, device=dev)   # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
