@@ -158,10 +158,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (HBM counter calibration)")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="instead of the attention benchmark, time the bf16 matrix-core calibration kernel "
-                         "(back-to-back 32x32x16 MFMAs on random N(0,1) operands from LDS, two waves per SIMD): "
-                         "the dense rate the chip sustains under its power limit")
+    ap.add_argument("--mfma-ceiling", nargs="?", const="bf16", default=None, choices=["bf16", "fp8"],
+                    help="instead of the attention benchmark, time the matrix-core calibration kernel "
+                         "(back-to-back MFMAs on random N(0,1) operands from LDS, two waves per SIMD; bf16: "
+                         "32x32x16, fp8: the scaled 32x32x64 with E4M3 operands): the dense rate the chip "
+                         "sustains under its power limit")
     ap.add_argument("--quantize", action="store_true",
                     help="instead of the attention benchmark, time the per-block E4M3 quantiser on the fp32 Q, K, V "
                          "of the fp8 workload (HBM-bound; reports GB/s)")
@@ -182,7 +183,7 @@ def main(argv=None):
     if args.copy_calibration > 0:
         return copy_calibration(args.copy_calibration, max(1, args.steps))
     if args.mfma_ceiling:
-        return bench_mfma_ceiling(args.steps, args.warmup, args.clock_settle)
+        return bench_mfma_ceiling(args.steps, args.warmup, args.clock_settle, args.mfma_ceiling)
     if args.quantize:
         return bench_quantize(args.steps, args.warmup, not args.no_cpu_baseline)
     if args.qknorm:
@@ -264,7 +265,7 @@ def copy_calibration(mib: int, reps: int) -> int:
     return 0
 
 
-def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float) -> int:
+def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float, kind: str = "bf16") -> int:
     """One step = one launch of the matrix-core calibration kernel on every CU."""
     import ctypes
 
@@ -276,20 +277,25 @@ def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float) -> int:
     if not os.path.exists(B.RATE_LIB):
         raise RuntimeError(f"calibration library not built: {B.RATE_LIB}")
     L = ctypes.CDLL(B.RATE_LIB)
-    L.attn_mfma_rate.restype = ctypes.c_int
-    L.attn_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fp8 = kind == "fp8"
+    fn = L.attn_mfma_rate_fp8 if fp8 else L.attn_mfma_rate
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     g = torch.Generator().manual_seed(11)
-    table = torch.randn(32768, generator=g).to(torch.bfloat16).to(dev)
+    if fp8:   # E4M3 codes of N(0,1) values (finite: no NaN code)
+        table = torch.randn(65536, generator=g).to(torch.float8_e4m3fn).view(torch.uint8).to(dev)
+    else:
+        table = torch.randn(32768, generator=g).to(torch.bfloat16).to(dev)
     out = torch.empty(cus * 512, dtype=torch.float32, device=dev)
     iters = 2000
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        rc = L.attn_mfma_rate(table.data_ptr(), cus, iters, out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        rc = fn(table.data_ptr(), cus, iters, out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
         if rc != 0:
-            raise RuntimeError(f"attn_mfma_rate: {rc}")
+            raise RuntimeError(f"attn_mfma_rate ({kind}): {rc}")
 
     settled = settle_clock(step, settle_s)
     warmed = warm_up(step, warmup)
@@ -304,18 +310,20 @@ def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    flops = cus * 8 * 16 * iters * 32 * 32 * 16 * 2
+    kdepth, peak = (64, 5000.0) if fp8 else (16, 2500.0)
+    flops = cus * 8 * 16 * iters * 32 * 32 * kdepth * 2
     avg = float(np.mean(per))
     result = {
-        "metric": "dense bf16 MFMA rate on random operands (matrix-core calibration)",
+        "metric": f"dense {kind} MFMA rate on random operands (matrix-core calibration)",
         "value": round(flops / (wall / steps) / 1e12, 1), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": steps, "warmup": warmed, "ms_per_step": round(wall * 1e3 / steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8 e4m3" if fp8 else "bf16",
+        "data": "synthetic",
         "clock_settle": {"seconds": settle_s, "launches": settled},
-        "config": {"workload": "mfma_32x32x16_bf16_random_lds_operands", "cus": cus, "waves_per_simd": 2,
-                   "mfmas_per_wave": 16 * iters},
-        "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 1), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / 2500.0, 4), "traffic": None,
+        "config": {"workload": ("mfma_scale_32x32x64_e4m3" if fp8 else "mfma_32x32x16_bf16") + "_random_lds_operands",
+                   "cus": cus, "waves_per_simd": 2, "mfmas_per_wave": 16 * iters},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / peak, 4), "traffic": None,
                      "kernel": "mfma_rate_kernel", "avg_launch_us": round(avg * 1e3, 2),
                      "algorithmic_flop_per_launch": flops},
     }
