@@ -32,7 +32,8 @@ def build(out: str = LIB, extra: list[str] | None = None) -> str:
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     if out == LIB:
-        subprocess.run([hipcc, *HIPCC_FLAGS, RATE_SRC, "-o", RATE_LIB + ".tmp"], check=True)
+        subprocess.run([hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), RATE_SRC, "-o", RATE_LIB + ".tmp"],
+                       check=True)
         os.replace(RATE_LIB + ".tmp", RATE_LIB)
     return out
 

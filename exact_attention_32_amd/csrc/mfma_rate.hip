@@ -13,6 +13,8 @@
 
 #include <cstdint>
 
+#include "mfma_rate.h"
+
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -76,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const u32x4 *__rest
 
 }  // namespace
 
-// table: device pointer to 64 KiB of operand values (bf16 values, or E4M3 codes for fp8 = 1);
+// The entry points of include/mfma_rate.h.  table: device pointer to 64 KiB of operand values (bf16
+// values, or E4M3 codes for the fp8 kernel);
 // out: device float[grid * 512]; 16 * iters MFMAs per wave; grid = the CU count gives one
 // workgroup (two waves per SIMD) per CU.  Returns 0, 1 for bad arguments, or the hipError_t of
 // the launch.

@@ -39,6 +39,23 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), f"library does not export {n}"
 
 
+def test_rate_library_exports_its_header():
+    """The matrix-core calibration library exports what include/mfma_rate.h declares, and rejects
+    bad arguments before any launch."""
+    from exact_attention_32_amd import build as B
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mfma_rate.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+    assert names == ["attn_mfma_rate", "attn_mfma_rate_fp8"]
+    L = ctypes.CDLL(B.RATE_LIB)
+    for n in names:
+        f = getattr(L, n)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        assert f(None, 1, 1, P, None) == 1 and f(P, 1, 1, None, None) == 1
+        assert f(P, 0, 1, P, None) == 1 and f(P, 1, 0, P, None) == 1
+
+
 def test_status_strings(lib):
     for code in range(9):
         s = lib.attn_status_string(code)
