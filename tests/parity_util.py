@@ -59,13 +59,56 @@ def ulp_distance(a: np.ndarray, b: np.ndarray, dtype: str) -> np.ndarray:
     return np.abs(oa - ob)
 
 
-def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray, dtype: str):
+# E4M3 round-to-nearest: relative error at most 2^-4 for normal values (3 mantissa bits); a
+# subnormal (below 2^-6) is off by at most 2^-10 in absolute terms
+E4M3_REL = 2.0 ** -4
+E4M3_SUB_ABS = 2.0 ** -10
+FEW_KEYS = 16
+
+
+def fp8_few_key_tolerance(oracle, q, k, v, o_ref, causal: bool, scale: float):
+    """Per-element tolerance on O for the fp8 path's rows with fewer than FEW_KEYS visible keys,
+    from the rounding of the probabilities to E4M3 alone; NaN elsewhere (and None when no row is
+    that short).
+
+    With weights p_j (the exact softmax row, from the oracle) rounded to p_j (1 + e_j), |e_j| <= u,
+    the normalised result moves by sum_j p_j e_j (v_j - O) / sum_j p_j (1 + e_j), at most
+    u / (1 - u) * sum_j p_j |v_j - O| per output element; a subnormal probability adds at most
+    2^-10 over the row's probability mass, which the first key tile puts at 2^5 or more, per key.
+    Over many keys these errors average out; over a handful they do not, and the literal fp8
+    tolerance is then below what any E4M3 rounding of P allows.  The bf16 rounding of O itself
+    (2^-9 relative) and 1e-4 of accumulation slack are added."""
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    nvis = np.array([min(i + 1, Sk) if causal else Sk for i in range(Sq)])
+    short = np.nonzero(nvis < FEW_KEYS)[0]
+    if short.size == 0:
+        return None
+    tol = np.full(o_ref.shape, np.nan)
+    i0, nr = int(short.min()), int(short.max() - short.min() + 1)
+    u = E4M3_REL
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        P = oracle.softmax_block(q, k, causal, scale, bh, i0, nr)
+        for i in short:
+            n = int(nvis[i])
+            dev = np.abs(v[b, h, :n] - o_ref[b, h, i][None, :])
+            rounding = u / (1.0 - u) * (P[i - i0, :n, None] * dev).sum(0)
+            sub = n * (E4M3_SUB_ABS / 32.0) * dev.max(0)
+            tol[b, h, i] = rounding + sub + 2.0 ** -9 * np.abs(o_ref[b, h, i]) + 1e-4
+    return tol
+
+
+def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray, dtype: str,
+            few_key_tol: np.ndarray | None = None):
     """Error statistics and the pass decision.
 
     Gate, per element of O: |O - O_ref| <= tol (1e-2 for f16/bf16, 5e-2 for fp8), or else O is
     within one ulp of the correctly rounded value RN(O_ref).  The second case is counted, in two
     classes: RN(O_ref) itself misses tol (bf16 spacing is 2^-6 in [2, 4) and 2^-5 in [4, 8), so no
     output of the type meets tol there), or RN(O_ref) meets tol and O is its neighbour.
+    few_key_tol (fp8 only, see fp8_few_key_tolerance): where finite and above tol, the tolerance of
+    that element; elements that pass only by it are counted.
     LSE: max |LSE - LSE_ref| <= 1e-3.  The raw max |O - O_ref| and the rounding floor are reported.
     """
     tol = TOL_O[dtype]
@@ -73,6 +116,10 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
     floor = rounding_floor(o_ref, dtype)
     lerr = np.abs(lse_gpu - lse_ref)
     over = err > tol
+    few_key = np.zeros_like(over)
+    if few_key_tol is not None:
+        few_key = over & np.isfinite(few_key_tol) & (err <= np.where(np.isfinite(few_key_tol), few_key_tol, 0.0))
+        over = over & ~few_key
     rounded = torch.from_numpy(np.ascontiguousarray(o_ref)).to(_OUT_DT[dtype]).double().numpy()
     one_ulp = over & (ulp_distance(o_gpu, rounded, dtype) <= 1)
     failed = over & ~one_ulp
@@ -85,6 +132,7 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
         "n_one_ulp_rn_misses_tol": int((one_ulp & (floor > tol)).sum()),
         "n_one_ulp_neighbour": int((one_ulp & (floor <= tol)).sum()),
         "n_failed": int(failed.sum()),
+        "n_fp8_few_key_rounding": int(few_key.sum()),
         "max_abs_err_LSE": float(lerr.max()) if lerr.size else 0.0,
         "finite": bool(np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))),
     }
