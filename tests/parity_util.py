@@ -109,7 +109,8 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
     output of the type meets tol there), or RN(O_ref) meets tol and O is its neighbour.
     few_key_tol (fp8 only, see fp8_few_key_tolerance): where finite and above tol, the tolerance of
     that element; elements that pass only by it are counted.
-    LSE: max |LSE - LSE_ref| <= 1e-3.  The raw max |O - O_ref| and the rounding floor are reported.
+    LSE: max |LSE - LSE_ref| <= 1e-3.  The raw max |O - O_ref| (and where it is: the (b, h, i, t) index),
+    the mean and RMS error and the rounding floor are reported.
     """
     tol = TOL_O[dtype]
     err = np.abs(o_gpu - o_ref)
@@ -125,6 +126,8 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
     failed = over & ~one_ulp
     stats = {
         "max_abs_err_O": float(err.max()) if err.size else 0.0,
+        "worst_O_at": tuple(int(i) for i in np.unravel_index(int(np.argmax(err)), err.shape)) if err.size else None,
+        "mean_abs_err_O": float(err.mean()) if err.size else 0.0,
         "rms_err_O": float(np.sqrt(np.mean(err ** 2))) if err.size else 0.0,
         "floor_O": float(floor.max()) if floor.size else 0.0,
         "n_elements": int(err.size),
