@@ -3,7 +3,8 @@
 One step = one attention forward (one kernel launch) over the whole batch of
 the workload, inputs already resident in HBM.  Prints ONE JSON line:
   value   : algorithmic TFLOP/s (4*d FLOP per visible (query, key) pair) over
-            exactly --steps launches, timed between device synchronisations;
+            exactly --steps launches (default: at least 100, and at least 0.2 s of
+            launches), timed between device synchronisations;
   roofline: the kernel's average launch duration from HIP events recorded on
             the stream it is launched on, against MI355X dense MFMA peak
             (bf16/fp16 2.5 PFLOP/s, fp8 5.0 PFLOP/s); `traffic` is the HBM
@@ -33,6 +34,8 @@ DEFAULT_WORKLOAD = "bf16_b2_h16_s4096_d128"
 # 255 us from launch 120 on).  Before the warmup steps, the same launch runs for CLOCK_SETTLE_S so
 # that the timed steps see the clock a sustained workload runs at; the line reports it.
 CLOCK_SETTLE_S = 0.25
+MIN_STEPS = 100        # timed steps at least, by default
+MIN_TIMED_S = 0.2      # and at least this much timed launch time, by default
 WARMUP_SECONDS = 0.25
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "e5m2": 5000.0}
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_32_amd", "csrc", "attn_fwd.hip")
@@ -106,7 +109,10 @@ def warm_up(step, warmup: int) -> int:
             return n
 
 
-def run_gpu(work, x, steps: int, warmup: int, settle_s: float):
+def run_gpu(work, x, steps, warmup: int, settle_s: float):
+    """Settle the clock, warm up, then time `steps` launches (None: at least MIN_STEPS and enough for
+    MIN_TIMED_S of launches, from the duration of 20 untimed ones), each between HIP events on the
+    launch stream."""
     import torch
 
     import exact_attention_32_amd as ea
@@ -129,6 +135,14 @@ def run_gpu(work, x, steps: int, warmup: int, settle_s: float):
 
     settled = settle_clock(step, settle_s)
     warmed = warm_up(step, warmup)
+    if steps is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / 20
+        steps = max(MIN_STEPS, int(MIN_TIMED_S / per) + 1)
     stream = torch.cuda.current_stream(dev)   # the stream the kernel is launched on
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -147,7 +161,9 @@ def run_gpu(work, x, steps: int, warmup: int, settle_s: float):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps; default: at least %d, and enough for %.1f s of timed launches "
+                         "(the attention benchmark; the other modes default to %d)" % (MIN_STEPS, MIN_TIMED_S, MIN_STEPS))
     ap.add_argument("--warmup", type=int, default=-1,
                     help="untimed warmup steps; default: until %.2f s have passed (the clock ramp)" % WARMUP_SECONDS)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
@@ -176,18 +192,18 @@ def main(argv=None):
               "independent, so sharding heads over GPUs needs no communication, but no multi-GPU path is built.",
               file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < -1:
+    if (args.steps is not None and args.steps < 1) or args.warmup < -1:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
 
     if args.copy_calibration > 0:
-        return copy_calibration(args.copy_calibration, max(1, args.steps))
+        return copy_calibration(args.copy_calibration, max(1, args.steps or MIN_STEPS))
     if args.mfma_ceiling:
-        return bench_mfma_ceiling(args.steps, args.warmup, args.clock_settle, args.mfma_ceiling)
+        return bench_mfma_ceiling(args.steps or MIN_STEPS, args.warmup, args.clock_settle, args.mfma_ceiling)
     if args.quantize:
-        return bench_quantize(args.steps, args.warmup, not args.no_cpu_baseline)
+        return bench_quantize(args.steps or MIN_STEPS, args.warmup, not args.no_cpu_baseline)
     if args.qknorm:
-        return bench_qknorm(args.steps, args.warmup, not args.no_cpu_baseline)
+        return bench_qknorm(args.steps or MIN_STEPS, args.warmup, not args.no_cpu_baseline)
 
     import numpy as np
 
@@ -200,8 +216,9 @@ def main(argv=None):
     x = I.make_inputs(work)
 
     wall, per_launch, warmed, settled = run_gpu(work, x, args.steps, args.warmup, args.clock_settle)
+    steps = len(per_launch)
     flops = work.flops()
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = float(np.mean(per_launch))
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
@@ -216,7 +233,7 @@ def main(argv=None):
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": warmed,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
