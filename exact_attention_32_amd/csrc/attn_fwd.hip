@@ -46,6 +46,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -1763,6 +1764,21 @@ int policy_override() {
 // faster there, nor are 192- or 256-key tiles (one wave per SIMD: 27-38% slower).  Choosing the kernel variant at run time from a table
 // measured per shape and keyed on the device's compute-unit count is the runtime policy of the
 // FlashInfer KDA write-up (blog.secrett2633), its section 1 and its closing lessons.
+// Causal query tiles of a head cost 1, 2, .., n key-tile rows of work; paired (n-1-j, j) they cost
+// n+1 each (the middle tile of an odd n alone (n+1)/2).  Equal items fill the CUs in whole rounds,
+// so pairing pays only where its rounds come out full: the makespan estimate of the pairs (rounds
+// of n+1, two middle tiles to a slot) against that of single tiles taken heaviest first (the
+// longest tile or the work per CU, whichever is larger), within 2% (what the shared K/V reads
+// gain: bf16 causal B=1 H=32 S=8192 d=128, 497 -> 482 us at equal balance).
+bool pairs_well(long long bh, int n, int cus) {
+    if (n < 2) return false;
+    const long long slots = bh * (n / 2) + ((n & 1) ? (bh + 1) / 2 : 0);
+    const long long paired = (slots + cus - 1) / cus * (n + 1);
+    const long long total = bh * n * (long long)(n + 1) / 2;
+    const long long single = std::max<long long>(n, (total + cus - 1) / cus);
+    return paired * 50 <= single * 51;
+}
+
 void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
     pl->sched = ATTN_SCHED_CLASSIC;
     pl->qb = 1;
@@ -1773,7 +1789,17 @@ void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
     } else {
         pl->ns = 4;
         pl->bk = 64;
-        if ((long long)B * H * ((Sq + 511) / 512) >= device_info().cus) pl->qb = 2;
+        if ((long long)B * H * ((Sq + 511) / 512) >= device_info().cus) {
+            pl->qb = 2;
+            // causal: (2, 8, 4) measured faster with its tiles paired (B=1 H=16 S=16384: 586
+            // against 606 us for (1, 8, 2, 128)); unpaired, 128-key tiles with 32 queries per wave
+            // are 1.5% faster (627.0 against 636.7 us)
+            if (causal && !pairs_well((long long)B * H, (Sq + 511) / 512, device_info().cus)) {
+                pl->qb = 1;
+                pl->ns = 2;
+                pl->bk = 128;
+            }
+        }
     }
     // at most 128 query rows: 256-query workgroups would compute as many clamped rows as real
     // ones; 4 waves of 32 queries compute none (B=1 H=2 S=128 d=64: 7.4 vs 7.8 us per launch)
@@ -1800,11 +1826,11 @@ int make_plan(int B, int H, int Sq, int d, int causal, Plan *pl) {
     pl->block_q = pl->nw * pl->qb * 32;
     pl->block_k = pl->bk;
     pl->nqt = (Sq + pl->block_q - 1) / pl->block_q;
-    // Causal tiles go in pairs (nqt-1-j, j) when the pairs alone still give every CU a workgroup:
-    // the key tiles are then fetched about once per head instead of up to twice (bf16 causal
-    // B=1 H=32 S=8192 d=128: FETCH_SIZE 1.33x the algorithmic bytes unpaired).
+    // Causal tiles go in pairs (nqt-1-j, j) where that keeps the CUs as busy (pairs_well): the key
+    // tiles are then fetched about once per head instead of up to twice (bf16 causal B=1 H=32
+    // S=8192 d=128: FETCH_SIZE 1.43x the algorithmic bytes unpaired, 1.25x paired).
     const long long npair = (long long)B * H * ((pl->nqt + 1) / 2);
-    pl->pair = causal && pl->sched == ATTN_SCHED_CLASSIC && pl->nqt >= 2 && npair >= device_info().cus;
+    pl->pair = causal && pl->sched == ATTN_SCHED_CLASSIC && pairs_well((long long)B * H, pl->nqt, device_info().cus);
     const long long wg = pl->pair ? npair : (long long)pl->nqt * B * H;
     if (wg > INT_MAX) return ATTN_ERR_OVERFLOW;
     pl->num_wg = (int)wg;

@@ -243,9 +243,11 @@ const char *attn_status_string(int status);
  * writes queries per workgroup, keys per tile, waves per workgroup and the
  * workgroup count (0 when there are no query rows).  With n query tiles of
  * block_q rows per (batch, head), the count is B*H*n, except for causal f16 /
- * bf16 problems on the classic schedule where B*H*ceil(n/2) still reaches the
- * device's CU count: a workgroup then takes the query tiles n-1-j and j of one
- * head (their keys cost n+1 tiles between them).  Returns an attn_status
+ * bf16 problems on the classic schedule whose tiles pair up into whole rounds
+ * of the device's CUs (the pairs' estimated time within 2% of single tiles
+ * taken heaviest first): a workgroup then takes the query tiles n-1-j and j of
+ * one head (their keys cost n+1 tiles between them), B*H*ceil(n/2) in all.
+ * Returns an attn_status
  * (argument checks as attn_fwd; the CU count is queried once per device).
  */
 int attn_fwd_plan(int B, int H, int S_q, int S_k, int d, int causal, int dtype, int *block_q, int *block_k,

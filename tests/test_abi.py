@@ -226,14 +226,19 @@ def test_set_policy(lib):
 
 
 def test_plan_causal_pairs(lib):
-    """Causal problems whose tile pairs still give every CU a workgroup launch one per pair of
-    query tiles (n-1-j, j); smaller ones, non-causal ones and fp8 one per tile.  (Here, without a
+    """Causal problems whose tile pairs fill the CUs in whole rounds launch one workgroup per pair
+    of query tiles (n-1-j, j); others, non-causal ones and fp8 one per tile.  (Here, without a
     device, the CU count is the 256 the table was measured on.)"""
-    assert ea.plan(1, 32, 8192, 8192, 128, True) == (256, 128, 8, 32 * 16)
-    assert ea.plan(1, 16, 16384, 16384, 64, True) == (512, 64, 8, 16 * 16)
+    assert ea.plan(1, 32, 8192, 8192, 128, True) == (256, 128, 8, 32 * 16)   # 512 pairs: 2 rounds
+    assert ea.plan(1, 16, 16384, 16384, 64, True) == (512, 64, 8, 16 * 16)   # 256 pairs: 1 round
     assert ea.plan(2, 43, 1200, 1200, 128, True)[3] == 2 * 43 * 3   # 5 tiles: 2 pairs and 1 alone
+    assert ea.plan(2, 256, 1300, 900, 64, True) == (512, 64, 8, 2 * 256 * 2)   # 3 tiles: odd, paired
     assert ea.plan(1, 32, 8192, 8192, 128, False)[3] == 32 * 32
     assert ea.plan(1, 2, 1024, 1024, 128, True)[3] == 2 * 4   # 4 pairs would leave CUs idle
+    # 300 pairs would take two rounds where 600 single tiles balance in about 1.2
+    assert ea.plan(1, 20, 7680, 7680, 128, True)[3] == 20 * 30
+    # d = 64: the 64-query waves only where their tiles pair well, else 128-key tiles unpaired
+    assert ea.plan(1, 20, 15360, 15360, 64, True) == (256, 128, 8, 20 * 60)
     assert ea.plan(1, 32, 8192, 8192, 128, True, dtype=ea.ATTN_FP8_E4M3)[3] == 32 * 32
 
 
