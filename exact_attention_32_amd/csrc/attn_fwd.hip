@@ -1753,17 +1753,15 @@ int policy_override() {
 }
 
 // Tile policy, measured on MI355X (bf16 B=2 H=16 S=4096, B=4 H=16 S=2048 and causal B=1 H=32
-// S=8192 at d=128; causal B=1 H=16 S=16384 and B=1 H=2 S=128 at d=64).  d=128: the classic
-// schedule with 128-key tiles and two stages is 1.4-2.1% faster than the de-phased schedule on
-// 64-key tiles, which in turn is 1.5-2% faster than the classic schedule on 64-key tiles (causal
-// S=8192 with paired tiles: 495 us against 524 for (1, 8, 4, 64) and 564 de-phased).  d=64: the
-// classic schedule with 64 queries per wave (2, 8, 4) is 7% faster than with 32 (1, 8, 4) as
-// long as its 512-query workgroups fill the 256 CUs (slower on the tiny S=128 workload, which
-// they do not), causal too now that causal tiles go in pairs (B=1 H=16 S=16384: 586 against
-// 606 us for (1, 8, 2, 128), which had been 1.5% faster unpaired); the de-phased schedule is not
-// faster there, nor are 192- or 256-key tiles (one wave per SIMD: 27-38% slower).  Choosing the kernel variant at run time from a table
-// measured per shape and keyed on the device's compute-unit count is the runtime policy of the
-// FlashInfer KDA write-up (blog.secrett2633), its section 1 and its closing lessons.
+// S=8192 at d=128; B=1..4, H=8..40, S=2048..16384 causal and not, and B=1 H=2 S=128 at d=64).
+// d=128: the classic schedule with 128-key tiles and two stages is 1.4-2.1% faster than the
+// de-phased schedule on 64-key tiles, which in turn is 1.5-2% faster than the classic schedule on
+// 64-key tiles (causal S=8192 with paired tiles: 495 us against 524 for (1, 8, 4, 64) and 564
+// de-phased).  d=64: see the rule below; the de-phased schedule is not faster there, nor are
+// 192- or 256-key tiles (one wave per SIMD: 27-38% slower).  Choosing the kernel variant at run
+// time from a table measured per shape and keyed on the device's compute-unit count is the
+// runtime policy of the FlashInfer KDA write-up (blog.secrett2633), its section 1 and its closing
+// lessons.
 // Causal query tiles of a head cost 1, 2, .., n key-tile rows of work; paired (n-1-j, j) they cost
 // n+1 each (the middle tile of an odd n alone (n+1)/2).  Equal items fill the CUs in whole rounds,
 // so pairing pays only where its rounds come out full: the makespan estimate of the pairs (rounds
@@ -1787,18 +1785,31 @@ void choose_policy(int B, int H, int Sq, int d, int causal, Plan *pl) {
         pl->ns = 2;
         pl->bk = 128;
     } else {
-        pl->ns = 4;
-        pl->bk = 64;
-        if ((long long)B * H * ((Sq + 511) / 512) >= device_info().cus) {
+        // d = 64: 128-key tiles with 32 queries per wave, (1, 8, 2, 128), or 64-key tiles with 64
+        // queries per wave, (2, 8, 4, 64), 4% faster per query tile but half as many tiles, so it
+        // wins only where its rounds of workgroups come out as full (non-causal: rounds times the
+        // tile's cost; B=2 H=16 S=4096 147.6 against 154.3 us, B=1 H=20 S=8192 525.3 against
+        // 423.5 us, its 320 tiles taking 2 rounds of 512 queries where (1, 8, 2, 128)'s 640 take 3
+        // rounds of 256).  Causal,
+        // it wins on long sequences with its tiles paired (B=1 H=16 S=16384: 586 against 606 us)
+        // and loses on short ones (B=4 H=32 S=2048: 104.9 against 97.6 us).  (1, 8, 4, 64) measured
+        // slower than (1, 8, 2, 128) on every d = 64 shape timed (B=1 H=8..40, S=2048..8192).
+        pl->ns = 2;
+        pl->bk = 128;
+        const long long bh = (long long)B * H, cus = device_info().cus;
+        const long long n512 = (Sq + 511) / 512, n256 = (Sq + 255) / 256;
+        bool wide;
+        if (!causal) {
+            const double t512 = (double)((bh * n512 + cus - 1) / cus) * 512.0;
+            const double t256 = (double)((bh * n256 + cus - 1) / cus) * 256.0 / 0.96;
+            wide = t512 <= t256;
+        } else {
+            wide = Sq >= 8192 && pairs_well(bh, (int)n512, (int)cus);
+        }
+        if (wide) {
             pl->qb = 2;
-            // causal: (2, 8, 4) measured faster with its tiles paired (B=1 H=16 S=16384: 586
-            // against 606 us for (1, 8, 2, 128)); unpaired, 128-key tiles with 32 queries per wave
-            // are 1.5% faster (627.0 against 636.7 us)
-            if (causal && !pairs_well((long long)B * H, (Sq + 511) / 512, device_info().cus)) {
-                pl->qb = 1;
-                pl->ns = 2;
-                pl->bk = 128;
-            }
+            pl->ns = 4;
+            pl->bk = 64;
         }
     }
     // at most 128 query rows: 256-query workgroups would compute as many clamped rows as real

@@ -217,12 +217,19 @@ def test_set_policy(lib):
     # the measured table: d = 128 takes 128-key tiles
     assert ea.plan(2, 16, 4096, 4096, 128, False)[:3] == (256, 128, 8)
     assert ea.kernel_name(128, False, ea.ATTN_BF16) == "attn_fwd_kernel"
-    # d = 64: 64 queries per wave once the 512-query workgroups fill the 256 CUs, causal or not
-    assert ea.plan(1, 16, 16384, 16384, 64, False)[:3] == (512, 64, 8)
+    # d = 64: 64 queries per wave where their 512-query workgroups come out in rounds at least as
+    # full as those of 256-query ones (non-causal) or pair into full rounds on long sequences
+    # (causal); else 128-key tiles with 32 queries per wave
+    assert ea.plan(1, 16, 16384, 16384, 64, False)[:3] == (512, 64, 8)   # 2 rounds against 4
+    assert ea.plan(2, 16, 4096, 4096, 64, False)[:3] == (512, 64, 8)     # 1 round against 2
+    assert ea.plan(1, 20, 8192, 8192, 64, False)[:3] == (256, 128, 8)    # 2 rounds against 3
+    assert ea.plan(1, 8, 8192, 8192, 64, False)[:3] == (256, 128, 8)     # 1 round either way
     assert ea.plan(1, 16, 16384, 16384, 64, True)[:3] == (512, 64, 8)
+    assert ea.plan(4, 32, 2048, 2048, 64, True)[:3] == (256, 128, 8)
+    assert ea.plan(1, 8, 8192, 8192, 64, True)[:3] == (256, 128, 8)
     # at most 128 query rows: 128-query workgroups (no clamped rows computed)
     assert ea.plan(1, 2, 128, 128, 64, False)[:3] == (128, 64, 4)
-    assert ea.plan(1, 2, 129, 128, 64, False)[:3] == (256, 64, 8)
+    assert ea.plan(1, 2, 129, 128, 64, False)[:3] == (256, 128, 8)
 
 
 def test_plan_causal_pairs(lib):
@@ -232,12 +239,12 @@ def test_plan_causal_pairs(lib):
     assert ea.plan(1, 32, 8192, 8192, 128, True) == (256, 128, 8, 32 * 16)   # 512 pairs: 2 rounds
     assert ea.plan(1, 16, 16384, 16384, 64, True) == (512, 64, 8, 16 * 16)   # 256 pairs: 1 round
     assert ea.plan(2, 43, 1200, 1200, 128, True)[3] == 2 * 43 * 3   # 5 tiles: 2 pairs and 1 alone
-    assert ea.plan(2, 256, 1300, 900, 64, True) == (512, 64, 8, 2 * 256 * 2)   # 3 tiles: odd, paired
+    assert ea.plan(2, 256, 1300, 900, 64, True) == (256, 128, 8, 2 * 256 * 3)   # 6 tiles: 3 pairs
     assert ea.plan(1, 32, 8192, 8192, 128, False)[3] == 32 * 32
     assert ea.plan(1, 2, 1024, 1024, 128, True)[3] == 2 * 4   # 4 pairs would leave CUs idle
     # 300 pairs would take two rounds where 600 single tiles balance in about 1.2
     assert ea.plan(1, 20, 7680, 7680, 128, True)[3] == 20 * 30
-    # d = 64: the 64-query waves only where their tiles pair well, else 128-key tiles unpaired
+    # d = 64: 30 tiles of 512 queries do not pair into full rounds, nor do 60 of 256
     assert ea.plan(1, 20, 15360, 15360, 64, True) == (256, 128, 8, 20 * 60)
     assert ea.plan(1, 32, 8192, 8192, 128, True, dtype=ea.ATTN_FP8_E4M3)[3] == 32 * 32
 

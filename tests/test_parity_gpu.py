@@ -136,6 +136,26 @@ def test_causal_pairs(oracle, shape, dtype):
     assert st["pass"], st
 
 
+@pytest.mark.parametrize("shape", [s for s in PAIRED if s[4] == 64], ids=lambda s: "x".join(map(str, s)))
+def test_causal_pairs_wide(oracle, shape):
+    """The d = 64 tiles of 64 queries per wave and 64 keys, paired: 4 query tiles a head (even)
+    and 3 (odd, the middle one alone)."""
+    import exact_attention_32_amd as ea
+
+    B, H, Sq, Sk, d = shape
+    ea.set_policy(ea.ATTN_SCHED_CLASSIC, 2, 8, 4, 64)
+    try:
+        bq, bk, w_, n = ea.plan(B, H, Sq, Sk, d, True)
+        nqt = -(-Sq // bq)
+        assert bq == 512 and n == B * H * ((nqt + 1) // 2), (shape, bq, n)
+        for dtype in ("bf16", "f16"):
+            w = I.random_workload(B, H, Sq, Sk, d, dtype, True, seed=4100 + Sq + 7 * Sk + H)
+            st = _run_full(oracle, w)
+            assert st["pass"], (dtype, st)
+    finally:
+        ea.set_policy(ea.ATTN_SCHED_DEFAULT)
+
+
 @pytest.mark.parametrize("kind", ["ramp12", "step40", "step150"])
 def test_causal_pairs_rising(oracle, kind):
     """Rising scores through paired causal tiles: the heavy tile raises its running max as the
@@ -143,7 +163,7 @@ def test_causal_pairs_rising(oracle, kind):
     import exact_attention_32_amd as ea
 
     dev = "cuda:0"
-    for d, dtype, S in ((64, "bf16", 2048), (128, "f16", 1024)):
+    for d, dtype, S in ((64, "bf16", 1024), (128, "f16", 1024)):
         q, k, v = _rising_inputs(kind, 1, 128, S, d, dtype, seed=d + 11)
         bq, _, _, n = ea.plan(1, 128, S, S, d, True)
         assert S // bq == 4 and n == 128 * 2   # four query tiles a head, in two pairs
