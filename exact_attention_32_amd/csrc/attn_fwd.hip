@@ -1261,6 +1261,9 @@ __device__ __forceinline__ f32x16 mfma_f8_sa(const i32x8 &a, const i32x8 &b, con
 // P' headroom: the tile that sets the running offset m puts its largest P' at 2^P8_HEAD (E4M3's
 // largest finite value is 448 = 2^8.81, its smallest subnormal 2^-9)
 constexpr float P8_HEAD = 5.0f;
+// the descale of a tensor passed without descales: its loads read this instead, so that the key
+// loop takes no branch on whether descales were given
+__constant__ float kUnitDescale = 1.0f;
 
 // four floats -> four E4M3 bytes (round to nearest even), first value in the low byte.  The
 // first conversion's "old" operand only supplies bytes 2-3, which the second one overwrites, so
@@ -1371,8 +1374,11 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
     typedef const __attribute__((address_space(4))) float cfloat;
     auto load_descales = [&](int t, float &kd, float &vd) __attribute__((always_inline)) {
         const int tt = min(t, p.nkb - 1);
-        kd = p.kd ? ((cfloat *)p.kd)[(size_t)bh * p.nkb + tt] : 1.f;
-        vd = p.vd ? ((cfloat *)p.vd)[(size_t)bh * p.nkb + tt] : 1.f;
+        const size_t i = (size_t)bh * p.nkb + tt;
+        cfloat *kp = p.kd ? (cfloat *)p.kd + i : (cfloat *)&kUnitDescale;
+        cfloat *vp = p.vd ? (cfloat *)p.vd + i : (cfloat *)&kUnitDescale;
+        kd = *kp;
+        vd = *vp;
     };
     float kd_cur, vd_cur;
 
@@ -1584,6 +1590,74 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
         }
     };
 
+    // P'(t-1) into O on the matrix core, interleaved in program order with the forming of P'(t)
+    // from the scores s of tile t (the VALU): P.V op j is issued after the j-th share of the
+    // exponentials, while the next share runs, and a scheduling fence after each keeps the pairs in
+    // that order.  Returns this lane's fp32 sum of p'(t); P'(t) goes to pnew.
+    auto pv_softmax = [&](const i32x8 (&pold)[BC / 64], uint32_t vt, int vsc, const f32x16 (&s)[BC / 32],
+                          const TileScale &ts, i32x8 (&pnew)[BC / 64]) __attribute__((always_inline)) {
+        uint32_t va[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            va[db] = vt + (uint32_t)vlane[db];
+            asm volatile("" : "+v"(va[db]));
+        }
+        constexpr int NPV = (BC / 64) * (D / 32), PV_AHEAD = 2;
+        constexpr int NGRP = (BC / 64) * 8, GPER = NGRP / NPV;   // groups of 4 scores per P.V op
+        static_assert(NGRP % NPV == 0, "shares");
+        auto pv_fetch = [&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value, kk = i / (D / 32), db = i % (D / 32);
+            const u32x2 r0 = lds_load_tr8<(64 * kk + 0) * ROWB>(va[db]);
+            const u32x2 r1 = lds_load_tr8<(64 * kk + 16) * ROWB>(va[db]);
+            const u32x2 r2 = lds_load_tr8<(64 * kk + 32) * ROWB>(va[db]);
+            const u32x2 r3 = lds_load_tr8<(64 * kk + 48) * ROWB>(va[db]);
+            return __builtin_bit_cast(i32x8, (u32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]});
+        };
+        const float off = ts.lvf - ((mrow == -INFINITY) ? 0.f : mrow);
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+        i32x8 ring[PV_AHEAD];
+        static_for<PV_AHEAD>([&](auto J) { ring[decltype(J)::value] = pv_fetch(J); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NPV>([&](auto J) {
+            constexpr int j = decltype(J)::value, kk = j / (D / 32), db = j % (D / 32);
+#pragma unroll
+            for (int gi = 0; gi < GPER; ++gi) {
+                const int grp = j * GPER + gi, k2 = grp >> 3, w = grp & 7;
+                const f32x16 &sv = s[2 * k2 + (w >> 2)];
+                const int o = 4 * (w & 3);
+                float e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    e[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[o + q], ts.ct, off));
+                    ls[q] += e[q];
+                }
+                pnew[k2][w] = pack4_e4m3(e[0], e[1], e[2], e[3]);
+            }
+            const i32x8 a = ring[j % PV_AHEAD];
+            if constexpr (j + PV_AHEAD < NPV) ring[j % PV_AHEAD] = pv_fetch(std::integral_constant<int, j + PV_AHEAD>{});
+            oacc[db] = mfma_f8_sa<FMT, 0>(a, pold[kk], oacc[db], vsc);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+
+    // A full tile past the first, with a tile waiting: the same steps with nothing left to decide
+    // at run time after the waiting tile's check, so that S^T(t), P'(t-1) into O and the forming of
+    // P'(t) fall in one basic block, with the P.V products interleaved into the softmax.
+    auto tile_steady = [&](int t) __attribute__((always_inline)) {
+        check_prev();
+        const TileScale ts = decode(kd_cur, vd_cur);
+        f32x16 s[BC / 32];
+        qk(s, stage(t), t, false);
+        i32x8 pnew[BC / 64];
+        ls_prev = pv_softmax(pprev, stage(t_prev) + TILEB, ts_prev.vsc, s, ts, pnew);
+        rs_prev = row_sum(pnew);
+#pragma unroll
+        for (int kk = 0; kk < BC / 64; ++kk) pprev[kk] = pnew[kk];
+        ts_prev = ts;
+        t_prev = t;
+    };
+
     // one iteration: wait until tile t has landed for every wave (this wave's loads of tile t+1 may
     // still be in flight), which also means every wave is done with iteration t-1 and so with tile
     // t-2, whose stage then receives tile t+2
@@ -1612,9 +1686,15 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(ParamsF8 p) {
     __builtin_amdgcn_s_waitcnt(0);
 
     int t = 0;
+    if (n_full > 0) {
+        step_begin(0);
+        tile(0, false, true);
+        load_descales(1, kd_cur, vd_cur);
+        t = 1;
+    }
     for (; t < n_full; ++t) {
         step_begin(t);
-        tile(t, false, true);
+        tile_steady(t);
         load_descales(t + 1, kd_cur, vd_cur);
     }
     // diagonal and tail tiles: a causal wave whose queries all precede the tile has nothing to add
