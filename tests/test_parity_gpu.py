@@ -250,9 +250,9 @@ def _rising_inputs(kind, B, H, S, d, dtype, seed, knoise=0.5):
     """Scores that grow along the keys, so the running max keeps moving: every query and key
     share a component along u = (1, ..., 1), with a key weight r_j.  In base-2 units the score
     is about r_j * sqrt(d) * log2(e) above the noise: 'ramp3' and 'ramp12' raise it by 3 and 12
-    per 128 keys; 'step20', 'step40' and 'step150' jump by that much at key 256 (past 2^15 a
-    probability does not fit f16, past 2^32 the kernel forms P again for bf16 too, and 2^150
-    overflows fp32, so p = exp2 of the score over a stale max is infinite there)."""
+    per 128 keys; 'step20', 'step40', 'step90' and 'step150' jump by that much at key 256 (past
+    2^15 a probability does not fit f16, past 2^64 the kernel forms P again for bf16 too, and
+    2^150 overflows fp32, so p = exp2 of the score over a stale max is infinite there)."""
     g = torch.Generator().manual_seed(seed)
     j = torch.arange(S, dtype=torch.float64)
     unit = float(np.sqrt(d) * np.log2(np.e))
@@ -272,7 +272,7 @@ def _rising_inputs(kind, B, H, S, d, dtype, seed, knoise=0.5):
 CLASSIC = [s for s in SCHEDULES if s[0] == 1]
 
 
-@pytest.mark.parametrize("kind", ["ramp3", "ramp12", "step20", "step40", "step150"])
+@pytest.mark.parametrize("kind", ["ramp3", "ramp12", "step20", "step40", "step90", "step150"])
 @pytest.mark.parametrize("sched", [None] + CLASSIC, ids=lambda s: "default" if s is None else "s%d_%d_%d_%d_%d" % s)
 def test_rising_scores(oracle, kind, sched):
     """Running max raised inside the key loop, by small and by overflowing steps, on every
@@ -298,6 +298,31 @@ def test_rising_scores(oracle, kind, sched):
                     assert st["pass"], (kind, sched, d, dtype, causal, st)
     finally:
         ea.set_policy(ea.ATTN_SCHED_DEFAULT)
+
+
+@pytest.mark.parametrize("scale_log2", [20, 40])
+def test_rising_scores_large_values(oracle, scale_log2):
+    """bf16: a step of 60 in base 2 (P up to 2^60 on the tile that moves the max: the deferred
+    factor, not a second pass) with V, then V scaled by 2^20 or 2^40, so that this tile's products
+    reach 2^106.  O is linear in V and every step of the kernel commutes with scaling V by a power
+    of two while nothing overflows, so the scaled output must be finite and exactly 2^s times the
+    unscaled one, which passes the gate against the oracle."""
+    import exact_attention_32_amd as ea
+
+    dev = "cuda:0"
+    for d in (64, 128):
+        for causal in (False, True):
+            q, k, v = _rising_inputs("step60", 1, 2, 700, d, "bf16", seed=d + 2 * causal + scale_log2)
+            vs = (v.double() * 2.0 ** scale_log2).to(torch.bfloat16)
+            U.say(f"[gpu] rising step60 V x 2^{scale_log2} d={d} causal={causal}")
+            o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=d ** -0.5)
+            o_s, lse_s = ea.fwd(q.to(dev), k.to(dev), vs.to(dev), causal=causal, scale=d ** -0.5)
+            torch.cuda.synchronize()
+            assert torch.isfinite(o_s).all()
+            assert torch.equal(o_s.double(), o.double() * 2.0 ** scale_log2) and torch.equal(lse_s, lse)
+            ro, rl = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, d ** -0.5)
+            st = U.compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "bf16")
+            assert st["pass"], (scale_log2, d, causal, st)
 
 
 @pytest.mark.parametrize("kind", ["ramp3", "ramp12", "step20", "step150"])
