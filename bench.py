@@ -174,10 +174,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (HBM counter calibration)")
-    ap.add_argument("--mfma-ceiling", nargs="?", const="bf16", default=None, choices=["bf16", "fp8"],
+    ap.add_argument("--mfma-ceiling", nargs="?", const="bf16", default=None, choices=["bf16", "fp8", "bf16-regs"],
                     help="instead of the attention benchmark, time the matrix-core calibration kernel "
                          "(back-to-back MFMAs on random N(0,1) operands from LDS, two waves per SIMD; bf16: "
-                         "32x32x16, fp8: the scaled 32x32x64 with E4M3 operands): the dense rate the chip "
+                         "32x32x16, fp8: the scaled 32x32x64 with E4M3 operands; bf16-regs: bf16 with the A operand "
+                         "in registers instead of LDS): the dense rate the chip "
                          "sustains under its power limit")
     ap.add_argument("--quantize", action="store_true",
                     help="instead of the attention benchmark, time the per-block E4M3 quantiser on the fp32 Q, K, V "
@@ -295,7 +296,8 @@ def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float, kind: str = "bf
         raise RuntimeError(f"calibration library not built: {B.RATE_LIB}")
     L = ctypes.CDLL(B.RATE_LIB)
     fp8 = kind == "fp8"
-    fn = L.attn_mfma_rate_fp8 if fp8 else L.attn_mfma_rate
+    regs = kind == "bf16-regs"
+    fn = L.attn_mfma_rate_fp8 if fp8 else (L.attn_mfma_rate_regs if regs else L.attn_mfma_rate)
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     dev = torch.device("cuda:0")
@@ -337,7 +339,8 @@ def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float, kind: str = "bf
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8 e4m3" if fp8 else "bf16",
         "data": "synthetic",
         "clock_settle": {"seconds": settle_s, "launches": settled},
-        "config": {"workload": ("mfma_scale_32x32x64_e4m3" if fp8 else "mfma_32x32x16_bf16") + "_random_lds_operands",
+        "config": {"workload": ("mfma_scale_32x32x64_e4m3" if fp8 else "mfma_32x32x16_bf16")
+                   + ("_random_register_operands" if regs else "_random_lds_operands"),
                    "cus": cus, "waves_per_simd": 2, "mfmas_per_wave": 16 * iters},
         "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / peak, 4), "traffic": None,

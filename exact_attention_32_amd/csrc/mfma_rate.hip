@@ -9,6 +9,10 @@
 //   bf16: v_mfma_f32_32x32x16_bf16, 16-byte A fragments; FLOP per MFMA = 32 * 32 * 16 * 2.
 //   fp8:  v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and unit block scales (the fp8
 //         attention kernel's instruction), 32-byte A fragments; FLOP per MFMA = 32 * 32 * 64 * 2.
+//   bf16, A in registers: the bf16 kernel with the A operand cycling through four register
+//         fragments (random values from the same table) instead of LDS reads, so that the rate
+//         with and without the attention kernels' 1 KiB of LDS operand reads per MFMA can be told
+//         apart.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -40,7 +44,7 @@ template <bool FP8> __device__ __forceinline__ f32x16 mfma_step(const u32x4 &a0,
     }
 }
 
-template <bool FP8>
+template <bool FP8, bool AREG = false>
 __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const u32x4 *__restrict__ table, int iters,
                                                              float *__restrict__ out) {
     // 96 KiB of LDS (the table in the first 64 KiB) keeps one workgroup per CU
@@ -50,6 +54,9 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const u32x4 *__rest
     u32x4 bq[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) bq[j] = table[(blockIdx.x * 64 + j * 512 + threadIdx.x) & (kTable16 - 1)];
+    u32x4 ar[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ar[j] = table[(blockIdx.x * 64 + j * 256 + 77 + threadIdx.x) & (kTable16 - 1)];
     __syncthreads();
     f32x16 acc[4];
 #pragma unroll
@@ -61,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const u32x4 *__rest
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const u32x4 a0 = lds[(base + u * 64) & (kTable16 - 1)];
+            const u32x4 a0 = AREG ? ar[u & 3] : lds[(base + u * 64) & (kTable16 - 1)];
             u32x4 a1 = a0;
             if constexpr (FP8) a1 = lds[(base + u * 64 + 32) & (kTable16 - 1)];
             acc[u & 3] = mfma_step<FP8>(a0, a1, bq[u & 7], bq[(u + 1) & 7], acc[u & 3]);
@@ -86,6 +93,13 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const u32x4 *__rest
 extern "C" int attn_mfma_rate(const void *table, int grid, int iters, float *out, void *stream) {
     if (!table || !out || grid < 1 || iters < 1) return 1;
     hipLaunchKernelGGL(mfma_rate_kernel<false>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4 *)table, iters, out);
+    return (int)hipGetLastError();
+}
+
+extern "C" int attn_mfma_rate_regs(const void *table, int grid, int iters, float *out, void *stream) {
+    if (!table || !out || grid < 1 || iters < 1) return 1;
+    hipLaunchKernelGGL((mfma_rate_kernel<false, true>), dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const u32x4 *)table, iters, out);
     return (int)hipGetLastError();
 }
