@@ -174,11 +174,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (HBM counter calibration)")
-    ap.add_argument("--mfma-ceiling", nargs="?", const="bf16", default=None, choices=["bf16", "fp8", "bf16-regs"],
+    ap.add_argument("--mfma-ceiling", nargs="?", const="bf16", default=None, choices=["bf16", "fp8", "bf16-regs", "fp8-regs"],
                     help="instead of the attention benchmark, time the matrix-core calibration kernel "
                          "(back-to-back MFMAs on random N(0,1) operands from LDS, two waves per SIMD; bf16: "
-                         "32x32x16, fp8: the scaled 32x32x64 with E4M3 operands; bf16-regs: bf16 with the A operand "
-                         "in registers instead of LDS): the dense rate the chip "
+                         "32x32x16, fp8: the scaled 32x32x64 with E4M3 operands; bf16-regs, fp8-regs: the same with the A "
+                         "operand in registers instead of LDS): the dense rate the chip "
                          "sustains under its power limit")
     ap.add_argument("--quantize", action="store_true",
                     help="instead of the attention benchmark, time the per-block E4M3 quantiser on the fp32 Q, K, V "
@@ -295,9 +295,10 @@ def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float, kind: str = "bf
     if not os.path.exists(B.RATE_LIB):
         raise RuntimeError(f"calibration library not built: {B.RATE_LIB}")
     L = ctypes.CDLL(B.RATE_LIB)
-    fp8 = kind == "fp8"
-    regs = kind == "bf16-regs"
-    fn = L.attn_mfma_rate_fp8 if fp8 else (L.attn_mfma_rate_regs if regs else L.attn_mfma_rate)
+    fp8 = kind.startswith("fp8")
+    regs = kind.endswith("-regs")
+    fn = {("bf16", False): L.attn_mfma_rate, ("bf16", True): L.attn_mfma_rate_regs,
+          ("fp8", False): L.attn_mfma_rate_fp8, ("fp8", True): L.attn_mfma_rate_fp8_regs}[("fp8" if fp8 else "bf16", regs)]
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     dev = torch.device("cuda:0")
@@ -333,7 +334,7 @@ def bench_mfma_ceiling(steps: int, warmup: int, settle_s: float, kind: str = "bf
     flops = cus * 8 * 16 * iters * 32 * 32 * kdepth * 2
     avg = float(np.mean(per))
     result = {
-        "metric": f"dense {kind} MFMA rate on random operands (matrix-core calibration)",
+        "metric": f"dense {'fp8' if fp8 else 'bf16'} MFMA rate on random operands (matrix-core calibration)",
         "value": round(flops / (wall / steps) / 1e12, 1), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": steps, "warmup": warmed, "ms_per_step": round(wall * 1e3 / steps, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8 e4m3" if fp8 else "bf16",

@@ -9,10 +9,9 @@
 //   bf16: v_mfma_f32_32x32x16_bf16, 16-byte A fragments; FLOP per MFMA = 32 * 32 * 16 * 2.
 //   fp8:  v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and unit block scales (the fp8
 //         attention kernel's instruction), 32-byte A fragments; FLOP per MFMA = 32 * 32 * 64 * 2.
-//   bf16, A in registers: the bf16 kernel with the A operand cycling through four register
-//         fragments (random values from the same table) instead of LDS reads, so that the rate
-//         with and without the attention kernels' 1 KiB of LDS operand reads per MFMA can be told
-//         apart.
+//   A in registers (bf16 or fp8): the same kernels with the A operand cycling through four
+//         register fragments (random values from the same table) instead of LDS reads, so that the
+//         rate with and without the attention kernels' LDS operand reads can be told apart.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -70,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const u32x4 *__rest
         for (int u = 0; u < 16; ++u) {
             const u32x4 a0 = AREG ? ar[u & 3] : lds[(base + u * 64) & (kTable16 - 1)];
             u32x4 a1 = a0;
-            if constexpr (FP8) a1 = lds[(base + u * 64 + 32) & (kTable16 - 1)];
+            if constexpr (FP8) a1 = AREG ? ar[(u + 1) & 3] : lds[(base + u * 64 + 32) & (kTable16 - 1)];
             acc[u & 3] = mfma_step<FP8>(a0, a1, bq[u & 7], bq[(u + 1) & 7], acc[u & 3]);
         }
         base += 1024;
@@ -107,6 +106,13 @@ extern "C" int attn_mfma_rate_regs(const void *table, int grid, int iters, float
 extern "C" int attn_mfma_rate_fp8(const void *table, int grid, int iters, float *out, void *stream) {
     if (!table || !out || grid < 1 || iters < 1) return 1;
     hipLaunchKernelGGL(mfma_rate_kernel<true>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4 *)table, iters, out);
+    return (int)hipGetLastError();
+}
+
+extern "C" int attn_mfma_rate_fp8_regs(const void *table, int grid, int iters, float *out, void *stream) {
+    if (!table || !out || grid < 1 || iters < 1) return 1;
+    hipLaunchKernelGGL((mfma_rate_kernel<true, true>), dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const u32x4 *)table, iters, out);
     return (int)hipGetLastError();
 }

@@ -34,6 +34,9 @@ int attn_mfma_rate_regs(const void *table, int grid, int iters, float *out, void
 /* v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 operands, unit block scales */
 int attn_mfma_rate_fp8(const void *table, int grid, int iters, float *out, void *stream);
 
+/* the same with the A operand from registers (no LDS reads) */
+int attn_mfma_rate_fp8_regs(const void *table, int grid, int iters, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,7 +46,7 @@ def test_rate_library_exports_its_header():
 
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mfma_rate.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
-    assert names == ["attn_mfma_rate", "attn_mfma_rate_fp8", "attn_mfma_rate_regs"]
+    assert names == ["attn_mfma_rate", "attn_mfma_rate_fp8", "attn_mfma_rate_fp8_regs", "attn_mfma_rate_regs"]
     L = ctypes.CDLL(B.RATE_LIB)
     for n in names:
         f = getattr(L, n)
