@@ -195,7 +195,7 @@ def _random_shapes(n, seed):
     return out
 
 
-@pytest.mark.parametrize("case", _random_shapes(24, 2024), ids=lambda c: "%s_b%d_h%d_%dx%d_d%d%s" % (
+@pytest.mark.parametrize("case", _random_shapes(96, 2024), ids=lambda c: "%s_b%d_h%d_%dx%d_d%d%s" % (
     c[5], c[0], c[1], c[2], c[3], c[4], "_causal" if c[6] else ""))
 def test_random_shapes(oracle, case):
     """Every element against the oracle on seeded random shapes (the default policy)."""
