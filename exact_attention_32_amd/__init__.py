@@ -118,7 +118,15 @@ def _shapes(q, k, v):
 
 
 def _stream(dev):
+    """dev's current stream as the library's stream argument."""
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _call(dev, fn, *args):
+    """Run a library entry point on dev's current stream with dev the current device: the library
+    launches on the current device, whatever device the stream belongs to."""
+    with torch.cuda.device(dev):
+        return fn(*args, _stream(dev))
 
 
 def _check_buffer(t, name: str, shape, dtype, device):
@@ -161,9 +169,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_buffer(lse, "lse", (B, H, S_q), torch.float32, q.device)
-    rc = load_library().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                 lse.data_ptr() if lse is not None else None, B, H, S_q, S_k, d,
-                                 int(bool(causal)), float(scale), dt, _stream(q.device))
+    rc = _call(q.device, load_library().attn_fwd, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+               lse.data_ptr() if lse is not None else None, B, H, S_q, S_k, d,
+               int(bool(causal)), float(scale), dt)
     _check(rc)
     return out, lse
 
@@ -191,9 +199,9 @@ def fwd_qnorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rstd: torch.T
         lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check_buffer(lse, "lse", (B, H, S_q), torch.float32, q.device)
-    rc = load_library().attn_fwd_qnorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_rstd.data_ptr(), w_q.data_ptr(),
-                                       out.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, S_q,
-                                       S_k, d, int(bool(causal)), float(scale), dt, _stream(q.device))
+    rc = _call(q.device, load_library().attn_fwd_qnorm, q.data_ptr(), k.data_ptr(), v.data_ptr(), q_rstd.data_ptr(),
+               w_q.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, S_q,
+               S_k, d, int(bool(causal)), float(scale), dt)
     _check(rc)
     return out, lse
 
@@ -228,9 +236,9 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scal
         _check_buffer(lse, "lse", (B, H, S_q), torch.float32, q.device)
     L = load_library()
     entry = L.attn_fwd_fp8 if fmt == "e4m3" else L.attn_fwd_fp8_e5m2
-    rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
+    rc = _call(q.device, entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
                v_descale.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None, B, H, S_q, S_k,
-               d, int(bool(causal)), float(scale), _stream(q.device))
+               d, int(bool(causal)), float(scale))
     _check(rc)
     return out, lse
 
@@ -258,7 +266,7 @@ def quantize_fp8(x: torch.Tensor, fmt: str = "e4m3", codes: torch.Tensor | None 
     _check_buffer(descale, "descale", (B, H, (S + 127) // 128), torch.float32, x.device)
     L = load_library()
     entry = L.attn_quantize_e4m3 if fmt == "e4m3" else L.attn_quantize_e5m2
-    rc = entry(x.data_ptr(), dt, codes.data_ptr(), descale.data_ptr(), B, H, S, d, _stream(x.device))
+    rc = _call(x.device, entry, x.data_ptr(), dt, codes.data_ptr(), descale.data_ptr(), B, H, S, d)
     _check(rc)
     return codes, descale
 
@@ -280,10 +288,10 @@ def quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, fmt: str = "
     codes = tuple(torch.empty(t.shape, dtype=torch.uint8, device=t.device) for t in (q, k, v))
     descales = tuple(torch.empty((B, H, (s + 127) // 128), dtype=torch.float32, device=q.device)
                      for s in (S_q, S_k, S_k))
-    rc = load_library().attn_quantize_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dt,
-                                          ATTN_FP8_E4M3 if fmt == "e4m3" else ATTN_FP8_E5M2,
-                                          *[c.data_ptr() for c in codes], *[x.data_ptr() for x in descales],
-                                          B, H, S_q, S_k, d, _stream(q.device))
+    rc = _call(q.device, load_library().attn_quantize_qkv, q.data_ptr(), k.data_ptr(), v.data_ptr(), dt,
+               ATTN_FP8_E4M3 if fmt == "e4m3" else ATTN_FP8_E5M2,
+               *[c.data_ptr() for c in codes], *[x.data_ptr() for x in descales],
+               B, H, S_q, S_k, d)
     _check(rc)
     return codes, descales
 
@@ -321,8 +329,8 @@ def qk_rmsnorm(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.T
     for t, ref in ((q_out, q), (k_out, k)):
         if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or t.device != ref.device:
             raise ValueError("outputs must be contiguous tensors of the inputs' shape and dtype")
-    rc = load_library().attn_qk_rmsnorm(q.data_ptr(), k.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), q_out.data_ptr(),
-                                        k_out.data_ptr(), B, H, S_q, S_k, d, float(eps), dt, _stream(q.device))
+    rc = _call(q.device, load_library().attn_qk_rmsnorm, q.data_ptr(), k.data_ptr(), w_q.data_ptr(), w_k.data_ptr(),
+               q_out.data_ptr(), k_out.data_ptr(), B, H, S_q, S_k, d, float(eps), dt)
     _check(rc)
     return q_out, k_out
 
@@ -347,7 +355,7 @@ def qk_rmsnorm_split(q: torch.Tensor, k: torch.Tensor, w_k: torch.Tensor, eps: f
         k_out = k
     k_out = torch.empty_like(k) if k_out is None else k_out
     _check_buffer(k_out, "k_out", tuple(k.shape), k.dtype, k.device)
-    rc = load_library().attn_qk_rmsnorm_split(q.data_ptr(), k.data_ptr(), w_k.data_ptr(), q_rstd.data_ptr(),
-                                              k_out.data_ptr(), B, H, S_q, S_k, d, float(eps), dt, _stream(q.device))
+    rc = _call(q.device, load_library().attn_qk_rmsnorm_split, q.data_ptr(), k.data_ptr(), w_k.data_ptr(),
+               q_rstd.data_ptr(), k_out.data_ptr(), B, H, S_q, S_k, d, float(eps), dt)
     _check(rc)
     return q_rstd, k_out
