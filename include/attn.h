@@ -14,7 +14,8 @@
  *
  * Layout: q and o are [B][H][S_q][d]; k and v are [B][H][S_k][d]; lse is
  * [B][H][S_q] fp32.  All dense, row-major, d fastest.  All pointers are
- * device pointers.
+ * device pointers on the current HIP device, where the kernels are launched;
+ * `stream` must belong to that device.
  *
  * Ownership: the caller allocates and owns every buffer.  The library keeps no
  * per-call state, allocates nothing and is re-entrant.  Calls are asynchronous
