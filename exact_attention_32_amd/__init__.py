@@ -125,6 +125,8 @@ def _stream(dev):
 def _call(dev, fn, *args):
     """Run a library entry point on dev's current stream with dev the current device: the library
     launches on the current device, whatever device the stream belongs to."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return fn(*args, _stream(dev))
     with torch.cuda.device(dev):
         return fn(*args, _stream(dev))
 
